@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds no part of the GLA arithmetic: it only draws numbers and
+rounds them to the storage dtype.  Every tensor comes from
+numpy default_rng(SeedSequence([config_id, tensor_id])), drawn in float64,
+scaled, then rounded to fp32 and, where the storage is bf16, to bf16 with
+round-to-nearest-even.  Arrays are returned as float64 holding exactly the
+stored values, plus the storage dtype name, so the oracle (fp64) and the
+device see bit-identical inputs.
+
+Workload shapes follow the page "Beyond the KV cache: Training and serving
+i14's Laplace 3B linear attention model on AWS Trainium2 with native PyTorch"
+(16 heads, dk = 96 half-width queries/keys, dv = 192 full-width values,
+sequence 2,048 in 16 chunks of 128, serving at 1,280 concurrent sequences with
+24 layers).  The pages give no value distributions; the Gaussian recipes below
+are the synthetic stand-ins.
+"""
+import math
+
+import numpy as np
+
+# tensor ids inside a config's seed sequence
+TID = {"q": 1, "k": 2, "v": 3, "S0": 4, "dO": 5, "dS_T": 6, "S": 7}
+
+
+def rng(config_id, tensor_id):
+    return np.random.default_rng(np.random.SeedSequence([int(config_id), int(tensor_id)]))
+
+
+def round_f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_bits(x):
+    """float -> bf16 bit pattern (uint16), round-to-nearest-even via fp32."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f64(b):
+    u = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x):
+    return bf16_bits_to_f64(bf16_bits(x))
+
+
+def round_to(x, dtype):
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return round_f32(x)
+    raise ValueError(dtype)
+
+
+def normal(config_id, tensor_id, shape, scale=1.0, dtype="f32"):
+    x = rng(config_id, tensor_id).standard_normal(size=shape) * scale
+    return round_to(x, dtype)
+
+
+def lambda_log_spaced(H, lo, hi):
+    """Per-head decays whose log-decay rates -ln(lambda) are geometrically
+    spaced between -ln(lo) and -ln(hi) (both endpoints exact in fp64, then
+    rounded to fp32)."""
+    g0, g1 = -math.log(lo), -math.log(hi)
+    if H == 1:
+        gam = np.array([g0])
+    else:
+        gam = g0 * (g1 / g0) ** (np.arange(H) / (H - 1))
+    return round_f32(np.exp(-gam))
+
+
+def lambda_half_life_schedule(H, t_min, t_max):
+    """Decay schedule with half-lives geometrically spaced from t_min to t_max
+    tokens: lambda_h = 2^(-1/T_h), T_h = t_min (t_max/t_min)^(h/(H-1)).
+    (Reading of the page's section "Decay schedule", whose formula image is
+    lost; it reproduces the printed endpoints lambda_0 = 0.5, lambda_15 ~ 0.9997.)"""
+    h = np.arange(H)
+    th = t_min * (t_max / t_min) ** (h / (H - 1))
+    return round_f32(2.0 ** (-1.0 / th))
+
+
+def lambda_tiny(H):
+    return round_f32(1.0 - 2.0 ** (-(4.0 + np.arange(H))))
+
+
+# ---------------------------------------------------------------------------
+# workload configurations
+CONFIGS = {
+    "tiny": dict(cid=1, B=1, H=2, T=256, dk=16, dv=32, chunk=64, dtype="f32"),
+    "laplace": dict(cid=2, B=1, H=16, T=2048, dk=96, dv=192, chunk=128, dtype="bf16"),
+    "training": dict(cid=3, B=8, H=16, T=2048, dk=96, dv=192, chunk=128, dtype="bf16"),
+    "long": dict(cid=4, B=1, H=16, T=65536, dk=96, dv=192, chunk=128, dtype="bf16"),
+    "decode": dict(cid=5, N=1280, L=24, H=16, dk=96, dv=192, steps=64, dtype="bf16"),
+}
+
+
+def make_chunk_inputs(name, B=None, T=None, with_grad=False, s0=None):
+    """Inputs of a chunked config (optionally a B/T slice of the same recipe:
+    a slice draws its own numbers, it is not a view of the full tensors)."""
+    c = dict(CONFIGS[name])
+    if B is not None:
+        c["B"] = B
+    if T is not None:
+        c["T"] = T
+    cid, B, H, T, dk, dv, dt = c["cid"], c["B"], c["H"], c["T"], c["dk"], c["dv"], c["dtype"]
+    out = dict(cfg=c)
+    if name == "tiny":
+        sc = 1.0 / math.sqrt(dk)
+        out["q"] = normal(cid, TID["q"], (B, H, T, dk), sc, dt)
+        out["k"] = normal(cid, TID["k"], (B, H, T, dk), sc, dt)
+        out["v"] = normal(cid, TID["v"], (B, H, T, dv), sc, dt)
+        out["lam"] = lambda_tiny(H)
+        out["S0"] = None
+    elif name in ("laplace", "training"):
+        out["q"] = normal(cid, TID["q"], (B, H, T, dk), 1.0, dt)
+        out["k"] = normal(cid, TID["k"], (B, H, T, dk), 1.0 / math.sqrt(dk), dt)
+        out["v"] = normal(cid, TID["v"], (B, H, T, dv), 1.0, dt)
+        out["lam"] = lambda_log_spaced(H, 0.9, 0.999)
+        out["S0"] = normal(cid, TID["S0"], (B, H, dk, dv), 0.01, "f32")
+    elif name == "long":
+        sc = 1.0 / math.sqrt(dk)
+        out["q"] = normal(cid, TID["q"], (B, H, T, dk), sc, dt)
+        out["k"] = normal(cid, TID["k"], (B, H, T, dk), sc, dt)
+        out["v"] = normal(cid, TID["v"], (B, H, T, dv), sc, dt)
+        out["lam"] = lambda_log_spaced(H, 0.95, 0.9999)
+        out["S0"] = None
+    else:
+        raise ValueError(name)
+    if s0 == "zero":
+        out["S0"] = None
+    elif s0 == "random":
+        out["S0"] = normal(cid, TID["S0"], (B, H, dk, dv), 0.01 if dt == "bf16" else 0.5, "f32")
+    if with_grad:
+        out["dO"] = normal(cid, TID["dO"], (B, H, T, dv), 1.0, dt)
+        out["dS_T"] = None
+    return out
+
+
+def random_chunk_inputs(seed, B, H, T, dk, dv, dtype="f32", s0=True, dS_T=False, lam=None,
+                        scale=None):
+    """Generic seeded inputs for edge-case tests (seed plays the config id)."""
+    sc = scale if scale is not None else 1.0 / math.sqrt(dk)
+    out = dict(
+        q=normal(seed, TID["q"], (B, H, T, dk), sc, dtype),
+        k=normal(seed, TID["k"], (B, H, T, dk), sc, dtype),
+        v=normal(seed, TID["v"], (B, H, T, dv), sc, dtype),
+        dO=normal(seed, TID["dO"], (B, H, T, dv), 1.0, dtype),
+        lam=round_f32(lam) if lam is not None else round_f32(
+            rng(seed, 99).uniform(0.5, 1.0, size=H)),
+        S0=normal(seed, TID["S0"], (B, H, dk, dv), 0.5, "f32") if s0 else None,
+        dS_T=normal(seed, TID["dS_T"], (B, H, dk, dv), 0.5, "f32") if dS_T else None,
+    )
+    return out

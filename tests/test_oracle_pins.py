@@ -1,0 +1,324 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+The page ("Beyond the KV cache ...", sections "GLA mixer", "Challenge 1",
+"Challenge 3") prints no worked numerical example, so the oracle is pinned by
+  * brute-force and closed forms (a different formula for the same quantity),
+  * textbook special cases evaluated with numpy (lambda = 1 is causal linear
+    attention, lambda = 0 keeps only the current token, k = 0 leaves the
+    decayed initial state, dk = dv = 1 with unit inputs is a geometric series),
+  * a hand-evaluated scalar example,
+  * invariants (chunk size, segment split / resume, decode = recurrence),
+  * exact finite differences for the backward (the loss is affine in each
+    input tensor taken alone, so central differences carry no truncation
+    error), and the backward's duality with the forward,
+  * the page's printed constants (decay-schedule endpoints, state sizes).
+Planted-mistake tests at the end show that plausible slips (readout before
+the update, decaying the new write, an off-by-one power) fail these pins.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_linear_attention_gla_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TIGHT = 1e-12
+
+
+def _inp(seed, B=2, H=3, T=50, dk=16, dv=32, **kw):
+    return inputs.random_chunk_inputs(seed, B, H, T, dk, dv, **kw)
+
+
+# --------------------------------------------------------------- forward pins
+@pytest.mark.parametrize("T", [1, 2, 17, 64, 100])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_recurrence_equals_bruteforce(T, with_s0):
+    x = _inp(10 + T, T=T, s0=with_s0)
+    o, _ = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    ob = oracle.fwd_bruteforce(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    assert oracle.rel_err(o, ob) <= TIGHT
+
+
+def test_recurrence_equals_bruteforce_full_head_dims():
+    x = _inp(3, B=1, H=2, T=64, dk=96, dv=192)
+    o, _ = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    ob = oracle.fwd_bruteforce(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    assert oracle.rel_err(o, ob) <= TIGHT
+
+
+@pytest.mark.parametrize("T", [1, 33, 128])
+def test_final_state_closed_form(T):
+    x = _inp(20 + T, T=T)
+    _, S = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    Sc = oracle.state_closed_form(x["k"], x["v"], x["lam"], x["S0"])
+    assert oracle.rel_err(S, Sc) <= TIGHT
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+@pytest.mark.parametrize("T", [1, 63, 65, 129, 256])
+def test_chunk_invariance(chunk, T):
+    x = _inp(30 + T, B=1, H=2, T=T)
+    o, S = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    oc, Sc = oracle.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], x["S0"], chunk=chunk)
+    assert oracle.rel_err(oc, o) <= TIGHT
+    assert oracle.rel_err(Sc, S) <= TIGHT
+
+
+def test_tiny_config_chunk_invariance():
+    """The tiny workload (B=1, H=2, T=256, dk=16, dv=32, fp32) at chunks 16/32/64."""
+    x = inputs.make_chunk_inputs("tiny")
+    o, S = oracle.fwd(x["q"], x["k"], x["v"], x["lam"])
+    ob = oracle.fwd_bruteforce(x["q"], x["k"], x["v"], x["lam"])
+    assert oracle.rel_err(o, ob) <= TIGHT
+    for c in (16, 32, 64):
+        oc, Sc = oracle.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], None, chunk=c)
+        assert oracle.rel_err(oc, o) <= TIGHT and oracle.rel_err(Sc, S) <= TIGHT
+
+
+def test_lambda_one_is_causal_linear_attention():
+    x = _inp(41, B=1, H=2, T=40, lam=np.ones(2))
+    q, k, v, S0 = x["q"], x["k"], x["v"], x["S0"]
+    o, S = oracle.fwd(q, k, v, x["lam"], S0)
+    for h in range(2):
+        Q, K, V = q[0, h], k[0, h], v[0, h]
+        ref = np.tril(Q @ K.T) @ V + Q @ S0[0, h]
+        assert oracle.rel_err(o[0, h], ref) <= TIGHT
+        assert oracle.rel_err(S[0, h], S0[0, h] + K.T @ V) <= TIGHT
+
+
+def test_lambda_zero_keeps_only_current_token():
+    x = _inp(42, B=1, H=2, T=30, lam=np.zeros(2))
+    q, k, v = x["q"], x["k"], x["v"]
+    o, S = oracle.fwd(q, k, v, x["lam"], x["S0"])
+    ref = np.einsum("bhtd,bhtd->bht", q, k)[..., None] * v
+    assert oracle.rel_err(o, ref) <= TIGHT
+    ref_S = np.einsum("bhd,bhe->bhde", k[:, :, -1], v[:, :, -1])
+    assert oracle.rel_err(S, ref_S) <= TIGHT
+
+
+def test_zero_keys_leave_decayed_initial_state():
+    x = _inp(43, B=1, H=3, T=25)
+    k0 = np.zeros_like(x["k"])
+    o, S = oracle.fwd(x["q"], k0, x["v"], x["lam"], x["S0"])
+    t = np.arange(1, 26)
+    for h in range(3):
+        w = x["lam"][h] ** t
+        ref = w[:, None] * (x["q"][0, h] @ x["S0"][0, h])
+        assert oracle.rel_err(o[0, h], ref) <= TIGHT
+        assert oracle.rel_err(S[0, h], x["lam"][h] ** 25 * x["S0"][0, h]) <= TIGHT
+
+
+@pytest.mark.parametrize("lam", [0.5, 0.9, 0.999])
+def test_geometric_series(lam):
+    """dk = dv = 1, q = k = v = 1, S0 = 0:  o_t = S_t = (1 - lam^t) / (1 - lam)."""
+    T = 40
+    one = np.ones((1, 1, T, 1))
+    o, S = oracle.fwd(one, one, one, np.array([lam]))
+    t = np.arange(1, T + 1)
+    ref = (1 - lam ** t) / (1 - lam)
+    assert np.max(np.abs(o[0, 0, :, 0] - ref)) <= 1e-13 * np.max(ref)
+    assert abs(S[0, 0, 0, 0] - ref[-1]) <= 1e-13 * ref[-1]
+
+
+def test_hand_worked_scalar_example():
+    """dk = dv = 1, lam = 0.5, S0 = 0.5, q = (1, 2, -1), k = (1, 1, 2), v = (2, -1, 1):
+    S1 = 0.5*0.5 + 1*2 = 2.25,    o1 = 1 * 2.25   = 2.25
+    S2 = 0.5*2.25 + 1*(-1) = 0.125, o2 = 2 * 0.125 = 0.25
+    S3 = 0.5*0.125 + 2*1 = 2.0625,  o3 = -1 * 2.0625 = -2.0625"""
+    q = np.array([1.0, 2.0, -1.0]).reshape(1, 1, 3, 1)
+    k = np.array([1.0, 1.0, 2.0]).reshape(1, 1, 3, 1)
+    v = np.array([2.0, -1.0, 1.0]).reshape(1, 1, 3, 1)
+    o, S = oracle.fwd(q, k, v, np.array([0.5]), np.array([[[[0.5]]]]))
+    assert np.array_equal(o.ravel(), [2.25, 0.25, -2.0625])
+    assert S.ravel()[0] == 2.0625
+
+
+def test_segment_split_resume():
+    x = _inp(44, B=2, H=2, T=90)
+    q, k, v, lam, S0 = x["q"], x["k"], x["v"], x["lam"], x["S0"]
+    o, S = oracle.fwd(q, k, v, lam, S0)
+    for T1 in (1, 37, 64, 89):
+        o1, S1 = oracle.fwd(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], lam, S0)
+        o2, S2 = oracle.fwd(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], lam, S1)
+        assert oracle.rel_err(np.concatenate([o1, o2], axis=2), o) <= TIGHT
+        assert oracle.rel_err(S2, S) <= TIGHT
+
+
+def test_decode_steps_equal_recurrence():
+    x = _inp(45, B=3, H=2, T=20)
+    q, k, v, lam, S0 = x["q"], x["k"], x["v"], x["lam"], x["S0"]
+    o, S = oracle.fwd(q, k, v, lam, S0)
+    St = S0.copy()
+    for t in range(20):
+        ot, St = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], lam, St)
+        assert oracle.rel_err(ot, o[:, :, t]) <= TIGHT
+    assert oracle.rel_err(St, S) <= TIGHT
+
+
+def test_empty_sequence_passes_state_through():
+    x = _inp(46, B=1, H=2, T=0)
+    o, S = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    assert o.shape == (1, 2, 0, 32)
+    assert np.array_equal(S, x["S0"])
+
+
+# -------------------------------------------------------------- backward pins
+def _loss(x, q=None, k=None, v=None, S0=None):
+    q = x["q"] if q is None else q
+    k = x["k"] if k is None else k
+    v = x["v"] if v is None else v
+    S0 = x["S0"] if S0 is None else S0
+    o, S = oracle.fwd(q, k, v, x["lam"], S0)
+    L = np.sum(x["dO"] * o)
+    if x["dS_T"] is not None:
+        L += np.sum(x["dS_T"] * S)
+    return L
+
+
+@pytest.mark.parametrize("with_dst", [False, True])
+def test_backward_equals_bruteforce(with_dst):
+    x = _inp(50, B=2, H=2, T=45, dS_T=with_dst)
+    g = oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"], x["dS_T"])
+    gb = oracle.bwd_bruteforce(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"], x["dS_T"])
+    for a, b in zip(g, gb):
+        assert oracle.rel_err(a, b) <= TIGHT
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "S0"])
+def test_backward_exact_finite_differences(which):
+    """L is affine in each input tensor alone: central differences are exact
+    up to fp64 rounding, for a random direction and for single coordinates."""
+    x = _inp(51, B=1, H=2, T=33, dS_T=True)
+    dq, dk, dv, dS0 = oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"], x["dS_T"])
+    grad = {"q": dq, "k": dk, "v": dv, "S0": dS0}[which]
+    base = x[which]
+    rng = np.random.default_rng(7)
+    eps = 0.25  # exactness does not depend on the step
+    delta = rng.standard_normal(base.shape)
+    fd = (_loss(x, **{which: base + eps * delta}) - _loss(x, **{which: base - eps * delta})) / (2 * eps)
+    an = np.sum(grad * delta)
+    assert abs(fd - an) <= 1e-10 * max(1.0, abs(an))
+    flat = base.reshape(-1)
+    for idx in rng.choice(flat.size, size=6, replace=False):
+        e = np.zeros_like(flat)
+        e[idx] = 1.0
+        e = e.reshape(base.shape)
+        fd = (_loss(x, **{which: base + eps * e}) - _loss(x, **{which: base - eps * e})) / (2 * eps)
+        assert abs(fd - grad.reshape(-1)[idx]) <= 1e-10 * max(1.0, abs(fd))
+
+
+def test_backward_slice_of_training_shape_fd():
+    """B=1, T=256 slice of the training-shape recipe (bf16 values, dk=96,
+    dv=192, 4 heads to bound the CPU time): directional FD for each input."""
+    x = inputs.make_chunk_inputs("training", B=1, T=256, with_grad=True)
+    x = {k: (v[:, :4] if isinstance(v, np.ndarray) and v.ndim == 4 else v) for k, v in x.items()}
+    x["lam"] = x["lam"][:4]
+    dq, dk, dv, dS0 = oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"])
+    rng = np.random.default_rng(8)
+    for which, grad in (("q", dq), ("k", dk), ("v", dv), ("S0", dS0)):
+        delta = rng.standard_normal(x[which].shape)
+        fd = (_loss(x, **{which: x[which] + delta}) - _loss(x, **{which: x[which] - delta})) / 2
+        an = np.sum(grad * delta)
+        assert abs(fd - an) <= 1e-9 * max(1.0, abs(an)), which
+
+
+def test_backward_duality_with_forward():
+    """dq is the forward recurrence with (q, k, v, S0) -> (dO, v, k, S0^T);
+    with dS_T = 0, dv and dk are time-reversed forwards and dS0 is lam times
+    the time-reversed closed-form state of (q, dO)."""
+    x = _inp(52, B=1, H=2, T=40)
+    q, k, v, lam, dO, S0 = x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"]
+    dq, dk, dv, dS0 = oracle.bwd(q, k, v, lam, dO, S0)
+    dq2, _ = oracle.fwd(dO, v, k, lam, np.swapaxes(S0, 2, 3))
+    assert oracle.rel_err(dq, dq2) <= TIGHT
+    r = lambda a: a[:, :, ::-1]
+    dv2, _ = oracle.fwd(r(k), r(q), r(dO), lam)
+    dk2, _ = oracle.fwd(r(v), r(dO), r(q), lam)
+    assert oracle.rel_err(dv, r(dv2)) <= TIGHT
+    assert oracle.rel_err(dk, r(dk2)) <= TIGHT
+    Sr = oracle.state_closed_form(r(q), r(dO), lam)
+    assert oracle.rel_err(dS0, lam[None, :, None, None] * Sr) <= TIGHT
+
+
+def test_backward_empty_sequence():
+    x = _inp(53, B=1, H=2, T=0, dS_T=True)
+    dq, dk, dv, dS0 = oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"], x["dS_T"])
+    assert np.array_equal(dS0, x["dS_T"])
+
+
+# ------------------------------------------------------------ page constants
+def test_decay_schedule_endpoints_from_page():
+    c = json.load(open(os.path.join(GOLDEN, "page_constants.json")))["decay_schedule"]
+    lam = inputs.lambda_half_life_schedule(c["H"], c["T_min"], c["T_max"])
+    assert lam[0] == c["lambda_0"]
+    assert abs(lam[-1] - c["lambda_15_approx"]) <= c["printed_precision_lambda_15"]
+    # half-lives: lam^T_h = 1/2
+    assert abs(lam[0] ** c["lambda_0_half_life_tokens"] - 0.5) < 1e-7
+    assert abs(lam[-1] ** c["lambda_15_half_life_tokens"] - 0.5) < 1e-3
+
+
+def test_state_size_from_page():
+    c = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    s, sv = c["state"], c["serving_state"]
+    per_layer = s["heads"] * s["dk"] * s["dv"] * 4  # fp32 state
+    total = s["layers"] * per_layer
+    conv = s["layers"] * 4 * s["hidden"] * 4  # width-4 causal conv window, fp32 (inferred)
+    assert abs((total + conv) / 1e6 - sv["mb_per_sequence"]) < 0.05
+    kv = 2 * s["layers"] * s["hidden"] * 2 * 8192  # bf16 K and V per layer at 8,192 tokens
+    assert abs(kv / (sv["mb_per_sequence"] * 1e6) - sv["kv_ratio_at_8192"]) < 0.5
+    ch = c["chunking"]
+    assert ch["num_chunks"] * ch["chunk"] == ch["seq_len"]
+
+
+def test_log_spaced_lambda_endpoints():
+    lam = inputs.lambda_log_spaced(16, 0.9, 0.999)
+    assert lam[0] == np.float32(0.9) and lam[-1] == np.float32(0.999)
+    g = -np.log(lam.astype(np.float64))
+    ratios = g[1:] / g[:-1]
+    assert np.max(np.abs(ratios - ratios[0])) < 1e-4  # fp32 rounding of lambda near 1
+
+
+# ---------------------------------------------- planted mistakes are caught
+def _mutant_fwd(q, k, v, lam, S0, kind):
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    S = np.zeros((B, H, dk, dv)) if S0 is None else S0.copy()
+    for t in range(T):
+        L = lam[None, :, None, None]
+        upd = np.einsum("bhd,bhe->bhde", k[:, :, t], v[:, :, t])
+        if kind == "readout_before_update":
+            o[:, :, t] = np.einsum("bhd,bhde->bhe", q[:, :, t], S)
+            S = L * S + upd
+            continue
+        if kind == "decay_new_write":
+            S = L * (S + upd)
+        else:
+            S = L * S + upd
+        o[:, :, t] = np.einsum("bhd,bhde->bhe", q[:, :, t], S)
+    return o, S
+
+
+@pytest.mark.parametrize("kind", ["readout_before_update", "decay_new_write"])
+def test_planted_mistakes_fail_pins(kind):
+    x = _inp(60, B=1, H=2, T=20)
+    om, Sm = _mutant_fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"], kind)
+    ob = oracle.fwd_bruteforce(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    Sc = oracle.state_closed_form(x["k"], x["v"], x["lam"], x["S0"])
+    assert oracle.rel_err(om, ob) > 1e-3 or oracle.rel_err(Sm, Sc) > 1e-3
+    # the unmutated numpy recurrence passes the same pins
+    og, Sg = _mutant_fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"], "none")
+    assert oracle.rel_err(og, ob) <= TIGHT and oracle.rel_err(Sg, Sc) <= TIGHT
+
+
+def test_planted_power_off_by_one_fails_geometric_series():
+    lam, T = 0.5, 10
+    t = np.arange(1, T + 1)
+    wrong = (1 - lam ** (t + 1)) / (1 - lam)  # an extra decay on the first write
+    one = np.ones((1, 1, T, 1))
+    o, _ = oracle.fwd(one, one, one, np.array([lam]))
+    assert np.max(np.abs(o[0, 0, :, 0] - wrong)) > 0.1
