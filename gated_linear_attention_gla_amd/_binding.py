@@ -1,0 +1,233 @@
+"""ctypes binding of libgla.so (argument marshalling only).
+
+Every entry point here forwards device pointers, strides and the current HIP
+stream to the C ABI declared in include/gla.h; all arithmetic runs in the HIP
+kernels.  PyTorch is used for device memory and streams.  If libgla.so is
+missing the calls raise: there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libgla.so")
+
+GLA_F32 = 0
+GLA_BF16 = 1
+
+STATUS_NAMES = {
+    0: "GLA_OK",
+    1: "GLA_ERR_NULL",
+    2: "GLA_ERR_SHAPE",
+    3: "GLA_ERR_STRIDE",
+    4: "GLA_ERR_DTYPE",
+    5: "GLA_ERR_UNSUPPORTED",
+    6: "GLA_ERR_ALIAS",
+    7: "GLA_ERR_WORKSPACE",
+    8: "GLA_ERR_HIP",
+}
+
+
+class GlaTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_t", ctypes.c_int64),
+    ]
+
+
+class GlaDims(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("dk", ctypes.c_int64),
+        ("dv", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
+    ]
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_LIB = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libgla.so and declare its signatures.  Raises if it is missing."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m gated_linear_attention_gla_amd.build)"
+        )
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.gla_abi_version.restype = ctypes.c_int
+    lib.gla_abi_version.argtypes = []
+    lib.gla_status_string.restype = ctypes.c_char_p
+    lib.gla_status_string.argtypes = [ctypes.c_int]
+    lib.gla_chunk_fwd_workspace.restype = ctypes.c_size_t
+    lib.gla_chunk_fwd_workspace.argtypes = [P(GlaDims)]
+    lib.gla_chunk_bwd_workspace.restype = ctypes.c_size_t
+    lib.gla_chunk_bwd_workspace.argtypes = [P(GlaDims)]
+    lib.gla_chunk_fwd.restype = ctypes.c_int
+    lib.gla_chunk_fwd.argtypes = [
+        P(GlaDims), P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp,
+        P(GlaTensor), vp, vp, ctypes.c_size_t, vp,
+    ]
+    lib.gla_chunk_bwd.restype = ctypes.c_int
+    lib.gla_chunk_bwd.argtypes = [
+        P(GlaDims), P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp,
+        P(GlaTensor), vp, P(GlaTensor), P(GlaTensor), P(GlaTensor), vp,
+        vp, ctypes.c_size_t, vp,
+    ]
+    lib.gla_decode_step.restype = ctypes.c_int
+    lib.gla_decode_step.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
+        P(GlaTensor), vp,
+    ]
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def _dtype_code(t):
+    if t == torch.float32:
+        return GLA_F32
+    if t == torch.bfloat16:
+        return GLA_BF16
+    raise TypeError(f"unsupported dtype {t}: use torch.bfloat16 or torch.float32")
+
+
+def _view4(x):
+    """(b, h, t, d) tensor -> GlaTensor (last dim must be contiguous)."""
+    if x.dim() != 4:
+        raise ValueError("expected a 4-D (b, h, t, d) tensor")
+    if x.numel() == 0:
+        return GlaTensor(None, _dtype_code(x.dtype), 0, 0, 0)
+    if x.shape[-1] > 1 and x.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    sb, sh, st, _ = x.stride()
+    return GlaTensor(x.data_ptr(), _dtype_code(x.dtype), sb, sh, st)
+
+
+def _view3(x):
+    """(n, h, d) tensor -> GlaTensor with stride_t unused."""
+    if x.dim() != 3:
+        raise ValueError("expected a 3-D (n, h, d) tensor")
+    if x.shape[-1] > 1 and x.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    sn, sh, _ = x.stride()
+    return GlaTensor(x.data_ptr(), _dtype_code(x.dtype), sn, sh, 0)
+
+
+def _ptr(x):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(lib, status):
+    if status != 0:
+        raise GlaError(status, lib.gla_status_string(status).decode())
+
+
+def _state_ok(S, B, H, dk, dv, name):
+    if S is None:
+        return
+    if S.dtype != torch.float32 or tuple(S.shape) != (B, H, dk, dv) or not S.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {(B, H, dk, dv)}")
+
+
+def chunk_fwd(q, k, v, lam, S0=None, chunk=128, out_dtype=None, o=None, S_T=None,
+              return_state=True):
+    """o, S_T = chunk_fwd(q, k, v, lam, S0): chunked Simple GLA forward.
+
+    q, k: (B, H, T, dk); v: (B, H, T, dv) device views (bf16 or fp32, last dim
+    contiguous); lam: float32 (H,); S0: float32 (B, H, dk, dv) or None.
+    """
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _state_ok(S0, B, H, dk, dv, "S0")
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=out_dtype or q.dtype, device=q.device)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    dims = GlaDims(B, H, T, dk, dv, chunk)
+    nws = lib.gla_chunk_fwd_workspace(ctypes.byref(dims))
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+    tq, tk, tv, to = _view4(q), _view4(k), _view4(v), _view4(o)
+    st = lib.gla_chunk_fwd(
+        ctypes.byref(dims), ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+        _ptr(lam), _ptr(S0), ctypes.byref(to), _ptr(S_T), _ptr(ws), nws, _stream(),
+    )
+    _check(lib, st)
+    return o, S_T
+
+
+def chunk_bwd(q, k, v, lam, dO, S0=None, dS_T=None, chunk=128, grad_dtype=None,
+              need_dS0=True, dq=None, dk=None, dv=None, dS0=None):
+    """dq, dk, dv, dS0 = chunk_bwd(...): gradients of sum <dO, o> + <dS_T, S_T>."""
+    lib = load_library()
+    B, H, T, DK = q.shape
+    DV = v.shape[-1]
+    _state_ok(S0, B, H, DK, DV, "S0")
+    _state_ok(dS_T, B, H, DK, DV, "dS_T")
+    gd = grad_dtype or q.dtype
+    if dq is None:
+        dq = torch.empty((B, H, T, DK), dtype=gd, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, H, T, DK), dtype=gd, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, H, T, DV), dtype=gd, device=q.device)
+    if dS0 is None and need_dS0:
+        dS0 = torch.empty((B, H, DK, DV), dtype=torch.float32, device=q.device)
+    dims = GlaDims(B, H, T, DK, DV, chunk)
+    nws = lib.gla_chunk_bwd_workspace(ctypes.byref(dims))
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+    views = [_view4(x) for x in (q, k, v, dO, dq, dk, dv)]
+    st = lib.gla_chunk_bwd(
+        ctypes.byref(dims), *(ctypes.byref(x) for x in views[:3]), _ptr(lam), _ptr(S0),
+        ctypes.byref(views[3]), _ptr(dS_T), *(ctypes.byref(x) for x in views[4:]),
+        _ptr(dS0), _ptr(ws), nws, _stream(),
+    )
+    _check(lib, st)
+    return dq, dk, dv, dS0
+
+
+def decode_step_(q, k, v, lam, S, o=None, out_dtype=None):
+    """o = decode_step_(q, k, v, lam, S): one recurrent step, S updated in place.
+
+    q, k: (N, H, dk); v: (N, H, dv); S: float32 (N, H, dk, dv) view whose heads
+    are dense (stride (S_stride_n, dk*dv, dv, 1)); returns o (N, H, dv).
+    """
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError("S must be float32 of shape (N, H, dk, dv)")
+    if S.stride()[1:] != (dk * dv, dv, 1):
+        raise ValueError("each sequence's heads must be dense in S")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype or q.dtype, device=q.device)
+    tq, tk, tv, to = _view3(q), _view3(k), _view3(v), _view3(o)
+    st = lib.gla_decode_step(
+        N, H, dk, dv, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(lam),
+        _ptr(S), S.stride(0), ctypes.byref(to), _stream(),
+    )
+    _check(lib, st)
+    return o

@@ -1,0 +1,228 @@
+// gla_api.cpp -- C ABI of libgla.so: argument validation and pass dispatch.
+//
+// Everything here runs on the host.  Each entry point checks all of its
+// arguments before touching the HIP runtime, so a rejected call enqueues
+// nothing (and can be exercised on a machine without a GPU).
+//
+// Backward passes.  For L = sum_t <dO_t, o_t> + <dS_T, S_T> (page "Beyond
+// the KV cache ...", section "Challenge 3": the backward runs through the
+// sequential state updates), with G_t = dL/dS_t:
+//   dq_t = S_t dO_t                       -- forward-time recurrence on S^T
+//   G_t  = lam G_{t+1} + q_t dO_t^T,  G_T = dS_T + q_T dO_T^T
+//   dv_t = G_t^T k_t,  dk_t = G_t v_t,  dS_0 = lam G_1
+// Each of dq, dv, dk is one chunked recurrence of the same form as the
+// forward with the roles of (q, k, v) permuted:
+//   dq: query dO, key v,  value k,  state S^T (starts at S0^T), forward time
+//   dv: query k,  key q,  value dO, state G   (starts at dS_T), reverse time
+//   dk: query v,  key dO, value q,  state G^T (starts at dS_T^T), reverse time
+// and the final state of the dv pass is dS0.
+#include "../../include/gla.h"
+#include "gla_internal.h"
+
+#include <stdint.h>
+
+using gla::ChunkArgs;
+using gla::DecodeArgs;
+
+namespace {
+
+int esize(int32_t dt) { return dt == GLA_F32 ? 4 : 2; }
+bool dtype_ok(int32_t dt) { return dt == GLA_F32 || dt == GLA_BF16; }
+
+// Row starts of a (b, h, t) view must be 16-byte aligned; strides that are
+// never stepped (size-1 dims) are not constrained.
+gla_status check_view(const gla_tensor* x, int64_t nb, int64_t nh, int64_t nt, bool need_data) {
+  if (need_data && x->data == nullptr) return GLA_ERR_NULL;
+  if (x->stride_b < 0 || x->stride_h < 0 || x->stride_t < 0) return GLA_ERR_STRIDE;
+  const int64_t es = esize(x->dtype);
+  if ((reinterpret_cast<uintptr_t>(x->data) & 15u) != 0) return GLA_ERR_STRIDE;
+  if (nb > 1 && (x->stride_b * es) % 16 != 0) return GLA_ERR_STRIDE;
+  if (nh > 1 && (x->stride_h * es) % 16 != 0) return GLA_ERR_STRIDE;
+  if (nt > 1 && (x->stride_t * es) % 16 != 0) return GLA_ERR_STRIDE;
+  return GLA_OK;
+}
+
+bool same(const void* a, const void* b) { return a != nullptr && a == b; }
+
+gla_status check_dims(const gla_dims* d) {
+  if (d->B < 1 || d->H < 1 || d->T < 0 || d->dk < 1 || d->dv < 1 || d->chunk < 1) return GLA_ERR_SHAPE;
+  if (d->B > (int64_t)1 << 24 || d->H > (int64_t)1 << 16 || d->T > (int64_t)1 << 40) return GLA_ERR_SHAPE;
+  if (d->B * d->H > (int64_t)1 << 26) return GLA_ERR_SHAPE;
+  return GLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ChunkArgs make_pass(const gla_dims* d, const gla_tensor* qr, const gla_tensor* kr, const gla_tensor* vr,
+                    const float* lambda, const float* s_init, int s_init_trans, float* s_final,
+                    gla_tensor* out, int reverse) {
+  ChunkArgs a{};
+  a.q = qr->data;
+  a.k = kr->data;
+  a.v = vr->data;
+  a.sq_b = qr->stride_b; a.sq_h = qr->stride_h; a.sq_t = qr->stride_t;
+  a.sk_b = kr->stride_b; a.sk_h = kr->stride_h; a.sk_t = kr->stride_t;
+  a.sv_b = vr->stride_b; a.sv_h = vr->stride_h; a.sv_t = vr->stride_t;
+  a.o = out->data;
+  a.so_b = out->stride_b; a.so_h = out->stride_h; a.so_t = out->stride_t;
+  a.lam = lambda;
+  a.s_init = s_init;
+  a.s_init_trans = s_init_trans;
+  a.s_final = s_final;
+  a.B = d->B; a.H = d->H; a.T = d->T;
+  a.reverse = reverse;
+  a.o_f32 = out->dtype == GLA_F32;
+  a.in_f32 = qr->dtype == GLA_F32;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_abi_version(void) { return GLA_ABI_VERSION; }
+
+const char* gla_status_string(gla_status s) {
+  switch (s) {
+    case GLA_OK: return "ok";
+    case GLA_ERR_NULL: return "a required pointer is NULL";
+    case GLA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case GLA_ERR_STRIDE: return "negative stride or misaligned row start (16 bytes required)";
+    case GLA_ERR_DTYPE: return "unknown dtype, or q/k/v/dO dtypes differ";
+    case GLA_ERR_UNSUPPORTED: return "no compiled kernel for this (dk, dv, chunk, dtype)";
+    case GLA_ERR_ALIAS: return "an output aliases an input or another output";
+    case GLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GLA_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+size_t gla_chunk_fwd_workspace(const gla_dims* dims) {
+  if (!dims || check_dims(dims) != GLA_OK) return 0;
+  return 0;
+}
+
+size_t gla_chunk_bwd_workspace(const gla_dims* dims) {
+  if (!dims || check_dims(dims) != GLA_OK) return 0;
+  return 0;
+}
+
+gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                         const gla_tensor* v, const float* lambda, const float* S0,
+                         gla_tensor* o, float* S_T, void* ws, size_t ws_bytes, void* stream) {
+  if (!dims || !q || !k || !v || !o || !lambda) return GLA_ERR_NULL;
+  gla_status st = check_dims(dims);
+  if (st != GLA_OK) return st;
+  const int64_t B = dims->B, H = dims->H, T = dims->T;
+  if (!dtype_ok(q->dtype) || !dtype_ok(o->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
+    return GLA_ERR_DTYPE;
+  const int in_f32 = q->dtype == GLA_F32;
+  if (!gla::chunk_pass_supported((int)dims->dk, (int)dims->dv, (int)dims->chunk, in_f32))
+    return GLA_ERR_UNSUPPORTED;
+  const bool need = T > 0;
+  if ((st = check_view(q, B, H, T, need)) != GLA_OK) return st;
+  if ((st = check_view(k, B, H, T, need)) != GLA_OK) return st;
+  if ((st = check_view(v, B, H, T, need)) != GLA_OK) return st;
+  if ((st = check_view(o, B, H, T, need)) != GLA_OK) return st;
+  if (!aligned16(S0) || !aligned16(S_T) || !aligned16(lambda)) return GLA_ERR_STRIDE;
+  if (same(o->data, q->data) || same(o->data, k->data) || same(o->data, v->data) ||
+      same(S_T, S0) || same(S_T, q->data) || same(S_T, k->data) || same(S_T, v->data) ||
+      same(S_T, o->data) || same(S_T, lambda) || same(o->data, lambda) || same(o->data, S0))
+    return GLA_ERR_ALIAS;
+  const size_t need_ws = gla_chunk_fwd_workspace(dims);
+  if (ws_bytes < need_ws || (need_ws > 0 && ws == nullptr)) return GLA_ERR_WORKSPACE;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, o, 0);
+  if (gla::launch_chunk_pass((int)dims->dk, (int)dims->dv, (int)dims->chunk, a, s) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                         const gla_tensor* v, const float* lambda, const float* S0,
+                         const gla_tensor* dO, const float* dS_T, gla_tensor* dq,
+                         gla_tensor* dk, gla_tensor* dv, float* dS0, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (!dims || !q || !k || !v || !lambda || !dO || !dq || !dk || !dv) return GLA_ERR_NULL;
+  gla_status st = check_dims(dims);
+  if (st != GLA_OK) return st;
+  const int64_t B = dims->B, H = dims->H, T = dims->T;
+  if (!dtype_ok(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype || dO->dtype != q->dtype ||
+      !dtype_ok(dq->dtype) || !dtype_ok(dk->dtype) || !dtype_ok(dv->dtype))
+    return GLA_ERR_DTYPE;
+  const int in_f32 = q->dtype == GLA_F32;
+  const int DK = (int)dims->dk, DV = (int)dims->dv, C = (int)dims->chunk;
+  if (!gla::chunk_pass_supported(DK, DV, C, in_f32) || !gla::chunk_pass_supported(DV, DK, C, in_f32))
+    return GLA_ERR_UNSUPPORTED;
+  const bool need = T > 0;
+  const gla_tensor* views[] = {q, k, v, dO, dq, dk, dv};
+  for (const gla_tensor* x : views)
+    if ((st = check_view(x, B, H, T, need)) != GLA_OK) return st;
+  if (!aligned16(S0) || !aligned16(dS_T) || !aligned16(dS0) || !aligned16(lambda)) return GLA_ERR_STRIDE;
+  const void* ins[] = {q->data, k->data, v->data, dO->data, lambda, S0, dS_T};
+  const void* outs[] = {dq->data, dk->data, dv->data, dS0};
+  for (int i = 0; i < 4; ++i) {
+    for (const void* p : ins)
+      if (same(outs[i], p)) return GLA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (same(outs[i], outs[j])) return GLA_ERR_ALIAS;
+  }
+  const size_t need_ws = gla_chunk_bwd_workspace(dims);
+  if (ws_bytes < need_ws || (need_ws > 0 && ws == nullptr)) return GLA_ERR_WORKSPACE;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // dq: query dO, key v, value k; state S^T from S0^T; forward time
+  ChunkArgs a1 = make_pass(dims, dO, v, k, lambda, S0, 1, nullptr, dq, 0);
+  if (gla::launch_chunk_pass(DV, DK, C, a1, s) != hipSuccess) return GLA_ERR_HIP;
+  // dv (and dS0): query k, key q, value dO; state G from dS_T; reverse time
+  ChunkArgs a2 = make_pass(dims, k, q, dO, lambda, dS_T, 0, dS0, dv, 1);
+  if (gla::launch_chunk_pass(DK, DV, C, a2, s) != hipSuccess) return GLA_ERR_HIP;
+  // dk: query v, key dO, value q; state G^T from dS_T^T; reverse time
+  ChunkArgs a3 = make_pass(dims, v, dO, q, lambda, dS_T, 1, nullptr, dk, 1);
+  if (gla::launch_chunk_pass(DV, DK, C, a3, s) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
+                           const gla_tensor* k, const gla_tensor* v, const float* lambda,
+                           float* S, int64_t S_stride_n, gla_tensor* o, void* stream) {
+  if (!q || !k || !v || !lambda || !S || !o) return GLA_ERR_NULL;
+  if (N < 1 || H < 1 || dk < 1 || dv < 1 || N > (int64_t)1 << 30 || H > (int64_t)1 << 16 ||
+      N * H > (int64_t)1 << 31)
+    return GLA_ERR_SHAPE;
+  if (!dtype_ok(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype || !dtype_ok(o->dtype))
+    return GLA_ERR_DTYPE;
+  if (!gla::decode_supported((int)dk, (int)dv)) return GLA_ERR_UNSUPPORTED;
+  if (S_stride_n < H * dk * dv) return GLA_ERR_SHAPE;
+  gla_status st;
+  // decode views are [N, H, d]: stride_b steps n, stride_h steps h
+  if ((st = check_view(q, N, H, 1, true)) != GLA_OK) return st;
+  if ((st = check_view(k, N, H, 1, true)) != GLA_OK) return st;
+  if ((st = check_view(v, N, H, 1, true)) != GLA_OK) return st;
+  if ((st = check_view(o, N, H, 1, true)) != GLA_OK) return st;
+  if (!aligned16(S) || !aligned16(lambda) || (N > 1 && (S_stride_n * 4) % 16 != 0)) return GLA_ERR_STRIDE;
+  const void* ins[] = {q->data, k->data, v->data, lambda};
+  for (const void* p : ins)
+    if (same(o->data, p) || same(S, p)) return GLA_ERR_ALIAS;
+  if (same(o->data, S)) return GLA_ERR_ALIAS;
+
+  DecodeArgs a{};
+  a.q = q->data; a.k = k->data; a.v = v->data;
+  a.sq_n = q->stride_b; a.sq_h = q->stride_h;
+  a.sk_n = k->stride_b; a.sk_h = k->stride_h;
+  a.sv_n = v->stride_b; a.sv_h = v->stride_h;
+  a.lam = lambda;
+  a.S = S;
+  a.S_stride_n = S_stride_n;
+  a.o = o->data;
+  a.so_n = o->stride_b; a.so_h = o->stride_h;
+  a.N = N; a.H = H;
+  a.o_f32 = o->dtype == GLA_F32;
+  a.in_f32 = q->dtype == GLA_F32;
+  if (gla::launch_decode((int)dk, (int)dv, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// gla_decode.hip -- single-token recurrent decode step, streaming fp32 states.
+//
+// Method: "Beyond the KV cache: Training and serving i14's Laplace 3B linear
+// attention model on AWS Trainium2 with native PyTorch", section "GLA mixer"
+// (fixed dk x dv state per head, so inference costs O(1) per token) and
+// section "Inference optimization on Trainium2" (the serving path reads and
+// writes one fixed-size recurrent state per sequence for each new token).
+//
+// Per (n, h):  S <- lam S + k v^T  (in place),  o = S^T q  (updated state).
+// The step is a pure HBM stream (each state is read once and written once),
+// so there is no MFMA: one workgroup owns one state; thread (cg, rp) owns the
+// four columns 4 cg..4 cg+3 and the rows rp, rp + RP, ...  A wavefront's
+// 16-byte accesses cover whole state rows, fully coalesced.  Column partial
+// sums of o are combined across the RP row phases through LDS.
+#include "gla_common.hpp"
+#include "gla_internal.h"
+
+namespace gla {
+
+template <int DK, int DV, int RP>
+__global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
+  constexpr int CG = DV / 4;          // float4 column groups
+  constexpr int NTHR = CG * RP;
+  constexpr int RPT = (DK + RP - 1) / RP;  // rows per thread
+  __shared__ float sq[DK];
+  __shared__ float sk[DK];
+  __shared__ float4 so[RP][CG];
+
+  const int64_t nh = blockIdx.x;
+  const int64_t n = nh / a.H;
+  const int64_t h = nh - n * a.H;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG;
+  const int rp = tid / CG;
+
+  if (tid < DK) {
+    const int64_t oq = n * a.sq_n + h * a.sq_h + tid;
+    const int64_t ok = n * a.sk_n + h * a.sk_h + tid;
+    if (a.in_f32) {
+      sq[tid] = reinterpret_cast<const float*>(a.q)[oq];
+      sk[tid] = reinterpret_cast<const float*>(a.k)[ok];
+    } else {
+      sq[tid] = bf16_to_f32(reinterpret_cast<const bf16_t*>(a.q)[oq]);
+      sk[tid] = bf16_to_f32(reinterpret_cast<const bf16_t*>(a.k)[ok]);
+    }
+  }
+  float4 vv;
+  {
+    const int64_t ov = n * a.sv_n + h * a.sv_h + 4 * cg;
+    if (a.in_f32) {
+      vv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.v) + ov);
+    } else {
+      const bf16_t* p = reinterpret_cast<const bf16_t*>(a.v) + ov;
+      vv = make_float4(bf16_to_f32(p[0]), bf16_to_f32(p[1]), bf16_to_f32(p[2]), bf16_to_f32(p[3]));
+    }
+  }
+  const float lam = a.lam[h];
+  f32x4* S = reinterpret_cast<f32x4*>(a.S + n * a.S_stride_n + h * (int64_t)DK * DV);
+
+  // issue every state load of this thread before the first use
+  f32x4 st[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int d = rp + i * RP;
+    if (d < DK) st[i] = __builtin_nontemporal_load(&S[d * CG + cg]);
+  }
+  __syncthreads();  // sq, sk ready
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int d = rp + i * RP;
+    if (d < DK) {
+      const float kd = sk[d], qd = sq[d];
+      f32x4 s = st[i];
+      s[0] = fmaf(lam, s[0], kd * vv.x);
+      s[1] = fmaf(lam, s[1], kd * vv.y);
+      s[2] = fmaf(lam, s[2], kd * vv.z);
+      s[3] = fmaf(lam, s[3], kd * vv.w);
+      __builtin_nontemporal_store(s, &S[d * CG + cg]);
+      acc.x = fmaf(qd, s[0], acc.x);
+      acc.y = fmaf(qd, s[1], acc.y);
+      acc.z = fmaf(qd, s[2], acc.z);
+      acc.w = fmaf(qd, s[3], acc.w);
+    }
+  }
+  so[rp][cg] = acc;
+  __syncthreads();
+  if (tid < CG) {
+    float4 r = so[0][tid];
+#pragma unroll
+    for (int p = 1; p < RP; ++p) {
+      const float4 u = so[p][tid];
+      r.x += u.x; r.y += u.y; r.z += u.z; r.w += u.w;
+    }
+    const int64_t oo = n * a.so_n + h * a.so_h + 4 * tid;
+    if (a.o_f32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + oo) = r;
+    } else {
+      bf16_t* p = reinterpret_cast<bf16_t*>(a.o) + oo;
+      p[0] = f32_to_bf16(r.x);
+      p[1] = f32_to_bf16(r.y);
+      p[2] = f32_to_bf16(r.z);
+      p[3] = f32_to_bf16(r.w);
+    }
+  }
+  (void)NTHR;
+}
+
+bool decode_supported(int dk, int dv) {
+  return (dk == 96 && dv == 192) || (dk == 16 && dv == 32);
+}
+
+hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st) {
+  const int64_t nblocks = a.N * a.H;
+  if (nblocks <= 0) return hipSuccess;
+  if (dk == 96 && dv == 192) {
+    hipLaunchKernelGGL((decode_kernel<96, 192, 4>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
+  } else if (dk == 16 && dv == 32) {
+    hipLaunchKernelGGL((decode_kernel<16, 32, 8>), dim3((unsigned)nblocks), dim3(8 * 8), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gla

@@ -1,0 +1,56 @@
+// gla_internal.h -- argument blocks and launcher declarations shared between
+// the host library (gla_api.cpp) and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+// One pass of the generic chunked recurrence over "roles" (qr, kr, vr):
+//   state  S (DK x DV, fp32, per (b, h)), decay lam[h]
+//   forward time:  S_t = lam S_{t-1} + kr_t vr_t^T,  out_t = S_t^T qr_t
+//   reverse time:  the same recurrence run from the last token to the first.
+// The chunked forward uses (q, k, v); the backward runs three passes with the
+// roles permuted (see gla_api.cpp).
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t sq_b, sq_h, sq_t;  // element strides of the query role
+  int64_t sk_b, sk_h, sk_t;
+  int64_t sv_b, sv_h, sv_t;
+  void* o;
+  int64_t so_b, so_h, so_t;
+  const float* lam;       // [H]
+  const float* s_init;    // [B][H] x (DK x DV) or null (zero state)
+  int s_init_trans;       // 1: element (d, n) stored at n * DK + d
+  float* s_final;         // [B][H][DK][DV] or null
+  int64_t B, H, T;
+  int reverse;            // 0: tokens 0..T-1, 1: tokens T-1..0
+  int o_f32;              // output storage: 1 fp32, 0 bf16
+  int in_f32;             // input storage:  1 fp32, 0 bf16 (must match the instantiation)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t sq_n, sq_h, sk_n, sk_h, sv_n, sv_h;
+  const float* lam;
+  float* S;
+  int64_t S_stride_n;  // elements between consecutive sequences; heads are dense
+  void* o;
+  int64_t so_n, so_h;
+  int64_t N, H;
+  int o_f32;
+  int in_f32;
+};
+
+// Launchers return hipSuccess or the launch error.  They perform no
+// validation: the C-ABI layer checks every argument first.
+hipError_t launch_chunk_pass(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st);
+bool chunk_pass_supported(int dk, int dv, int chunk, int in_f32);
+hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
+bool decode_supported(int dk, int dv);
+
+}  // namespace gla

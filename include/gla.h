@@ -1,0 +1,147 @@
+/*
+ * gla.h -- C ABI of the Simple GLA mixer library (libgla.so, AMD MI355X /
+ * gfx950).
+ *
+ * The operation is the token mixer described on the page "Beyond the KV
+ * cache: Training and serving i14's Laplace 3B linear attention model on AWS
+ * Trainium2 with native PyTorch":
+ *   - section "GLA mixer": every head h keeps a dk x dv matrix state that is
+ *     decayed by a fixed per-head factor lambda_h and receives the rank-1
+ *     write of the current key/value pair; the output queries the state:
+ *         S_t = lambda_h * S_{t-1} + k_t v_t^T,     o_t = S_t^T q_t
+ *     (the readout sees the updated state, so o_t includes token t itself);
+ *   - section "Challenge 1": the chunked form used for prefill and training
+ *     (masked linear attention inside each chunk plus the running state; the
+ *     state advances by the decay compounded over the chunk);
+ *   - section "Challenge 3": the backward pass through the sequential state
+ *     updates;
+ *   - sections "GLA mixer" and "Inference optimization on Trainium2": the
+ *     O(1)-per-token recurrent decode step against a fixed-size state.
+ *
+ * Conventions shared by every entry point
+ *   Ownership   The caller owns every buffer.  Pointers are HIP device
+ *               pointers unless stated otherwise.  The library never
+ *               allocates or frees; transient memory comes from the caller's
+ *               workspace, sized by the matching *_workspace() query.
+ *   Streams     `stream` is a hipStream_t passed as void* (NULL = the null
+ *               stream).  Every call only enqueues work and returns without
+ *               synchronising; buffers must stay valid until it completes.
+ *   Errors      All arguments are validated on the host before anything is
+ *               enqueued; on a non-OK status nothing was enqueued.  A launch
+ *               failure returns GLA_ERR_HIP.  Faults inside kernels surface at
+ *               the caller's next synchronisation.  No C++ exception crosses
+ *               the ABI.  Calls keep no global state and are thread-safe.
+ *   Tensors     gla_tensor describes a 4-D (b, h, t, d) view: element
+ *               (b, h, t, d) lives at data + (b*stride_b + h*stride_h +
+ *               t*stride_t + d) elements; d is contiguous.  Strides are in
+ *               elements, non-negative.  The base pointer and every row start
+ *               must be 16-byte aligned (GLA_ERR_STRIDE otherwise).  Both the
+ *               head-major [B,H,T,d] and the token-major [B,T,H,d] layouts
+ *               are accepted without copies.
+ *   Dtypes      q, k, v (and dO) share one dtype, GLA_BF16 or GLA_F32.
+ *               Outputs o, dq, dk, dv may each be GLA_BF16 or GLA_F32.  All
+ *               states (S0, S_T, dS_T, dS0, decode S) and lambda are fp32,
+ *               dense row-major [B][H][dk][dv] (dk rows of dv).
+ *   Shapes      (dk, dv) in {(96, 192), (16, 32)}; chunk in {16, 32, 64, 128}.
+ *               fp32 inputs at (96, 192) need chunk <= 64 for the forward and
+ *               chunk <= 32 for the backward.  Other combinations return
+ *               GLA_ERR_UNSUPPORTED.  B, H >= 1; T >= 0 (T = 0 copies the
+ *               state through); T need not be a multiple of chunk.
+ *   Decay       lambda[h] must satisfy 0 <= lambda[h] <= 1 (not checked on
+ *               the device); 0^0 is taken as 1.  NaN/Inf inputs propagate.
+ *   Aliasing    Outputs must not share a base pointer with any input or with
+ *               each other (GLA_ERR_ALIAS); the decode state is in/out.
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLA_ABI_VERSION 1
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  GLA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  GLA_ERR_STRIDE = 3,      /* negative stride or a misaligned row start */
+  GLA_ERR_DTYPE = 4,       /* unknown dtype or q/k/v dtypes differ */
+  GLA_ERR_UNSUPPORTED = 5, /* (dk, dv, chunk, dtype) has no compiled kernel */
+  GLA_ERR_ALIAS = 6,       /* an output aliases an input or another output */
+  GLA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
+  GLA_ERR_HIP = 8          /* the HIP runtime reported a launch error */
+} gla_status;
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+typedef struct {
+  void* data;
+  int32_t dtype; /* gla_dtype */
+  int64_t stride_b, stride_h, stride_t;
+} gla_tensor;
+
+typedef struct {
+  int64_t B, H, T, dk, dv, chunk;
+} gla_dims;
+
+/* ABI version of the loaded library (GLA_ABI_VERSION). */
+int gla_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gla_status_string(gla_status s);
+
+/* Bytes of device workspace gla_chunk_fwd needs for these dims (0 if none).
+ * Returns 0 for dims that gla_chunk_fwd would reject. */
+size_t gla_chunk_fwd_workspace(const gla_dims* dims);
+
+/* Chunked forward (page sections "GLA mixer" and "Challenge 1").
+ *   q [B,H,T,dk], k [B,H,T,dk], v [B,H,T,dv]   inputs (gla_tensor views)
+ *   lambda [H] fp32                            per-head decay
+ *   S0 [B,H,dk,dv] fp32 or NULL                state before token 1 (NULL = 0)
+ *   o [B,H,T,dv]                               output (bf16 or fp32)
+ *   S_T [B,H,dk,dv] fp32 or NULL               state after token T
+ *   ws, ws_bytes                               workspace (may be NULL if the
+ *                                              query returned 0)
+ * o_t = lambda^t S0^T q_t + sum_{s<=t} lambda^{t-s} (q_t . k_s) v_s. */
+gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                         const gla_tensor* v, const float* lambda, const float* S0,
+                         gla_tensor* o, float* S_T, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace gla_chunk_bwd needs (0 if none). */
+size_t gla_chunk_bwd_workspace(const gla_dims* dims);
+
+/* Chunked backward (page section "Challenge 3") of the scalar
+ *   L = sum_t <dO_t, o_t> + <dS_T, S_T>
+ * with o, S_T the forward outputs for the same (q, k, v, lambda, S0):
+ *   dO [B,H,T,dv]       upstream gradient of o (same dtype as q, k, v)
+ *   dS_T fp32 or NULL   upstream gradient of S_T (NULL = 0)
+ *   dq [B,H,T,dk], dk [B,H,T,dk], dv [B,H,T,dv]  outputs (bf16 or fp32)
+ *   dS0 [B,H,dk,dv] fp32 or NULL                 gradient of S0 (NULL = skip)
+ * lambda is fixed (not learned), so there is no gradient for it. */
+gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                         const gla_tensor* v, const float* lambda, const float* S0,
+                         const gla_tensor* dO, const float* dS_T, gla_tensor* dq,
+                         gla_tensor* dk, gla_tensor* dv, float* dS0, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* One recurrent decode step for N sequences x H heads (page sections "GLA
+ * mixer" and "Inference optimization on Trainium2"):
+ *   S <- lambda S + k v^T (in place),  then  o = S^T q.
+ *   q, k [N,H,dk]; v, o [N,H,dv]  gla_tensor views with stride_b = stride
+ *                                 over n, stride_h over h (stride_t unused)
+ *   S    fp32, sequence n / head h at S + n*S_stride_n + h*dk*dv, dense
+ *        dk x dv per head; S_stride_n >= H*dk*dv elements (a per-sequence
+ *        page may hold further layers' states), 16-byte aligned. */
+gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
+                           const gla_tensor* k, const gla_tensor* v, const float* lambda,
+                           float* S, int64_t S_stride_n, gla_tensor* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

@@ -1,0 +1,198 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol include/gla.h declares, and rejects bad arguments before anything is
+enqueued.  Every call below fails validation, so no kernel is ever launched;
+the fake device pointers are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_linear_attention_gla_amd import _binding as gb
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "gla.h")
+
+OK, NULL, SHAPE, STRIDE, DTYPE, UNSUP, ALIAS, WS, HIP = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gb.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("gla_chunk_fwd", "gla_chunk_bwd", "gla_decode_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gla_abi_version() == 1
+    for s in range(9):
+        assert lib.gla_status_string(s)
+    assert lib.gla_status_string(42) == b"unknown status"
+
+
+def T(ptr, dtype=gb.GLA_BF16, sb=0, sh=0, st=0):
+    return gb.GlaTensor(ptr, dtype, sb, sh, st)
+
+
+def dims(B=1, H=2, Tn=64, dk=96, dv=192, chunk=64):
+    return gb.GlaDims(B, H, Tn, dk, dv, chunk)
+
+
+def fwd(lib, d, q, k, v, o, lam=0x9000, S0=None, ST=None, ws=None, nws=0):
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    return lib.gla_chunk_fwd(ref(d), ref(q), ref(k), ref(v), lam, S0, ref(o), ST, ws, nws, None)
+
+
+def views(H=2, Tn=64, dk=96, dv=192):
+    # dense (1, H, T, d) bf16 views at distinct fake, aligned addresses
+    q = T(0x100000, sb=H * Tn * dk, sh=Tn * dk, st=dk)
+    k = T(0x200000, sb=H * Tn * dk, sh=Tn * dk, st=dk)
+    v = T(0x300000, sb=H * Tn * dv, sh=Tn * dv, st=dv)
+    o = T(0x400000, sb=H * Tn * dv, sh=Tn * dv, st=dv)
+    return q, k, v, o
+
+
+def test_fwd_null_and_shape(lib):
+    q, k, v, o = views()
+    assert fwd(lib, None, q, k, v, o) == NULL
+    assert fwd(lib, dims(), None, k, v, o) == NULL
+    assert fwd(lib, dims(), q, k, v, o, lam=None) == NULL
+    assert fwd(lib, dims(B=0), q, k, v, o) == SHAPE
+    assert fwd(lib, dims(H=0), q, k, v, o) == SHAPE
+    assert fwd(lib, dims(Tn=-1), q, k, v, o) == SHAPE
+
+
+def test_fwd_dtype(lib):
+    q, k, v, o = views()
+    k.dtype = gb.GLA_F32
+    assert fwd(lib, dims(), q, k, v, o) == DTYPE
+    q2, k2, v2, o2 = views()
+    o2.dtype = 7
+    assert fwd(lib, dims(), q2, k2, v2, o2) == DTYPE
+
+
+@pytest.mark.parametrize("dk,dv,chunk", [(64, 128, 64), (96, 96, 64), (96, 192, 48), (96, 192, 256),
+                                         (16, 32, 8)])
+def test_fwd_unsupported(lib, dk, dv, chunk):
+    q, k, v, o = views(dk=dk, dv=dv)
+    assert fwd(lib, dims(dk=dk, dv=dv, chunk=chunk), q, k, v, o) == UNSUP
+
+
+def test_fwd_fp32_large_chunk_unsupported(lib):
+    q, k, v, o = views()
+    for x in (q, k, v):
+        x.dtype = gb.GLA_F32
+    assert fwd(lib, dims(chunk=128), q, k, v, o) == UNSUP
+
+
+def test_fwd_stride_checks(lib):
+    q, k, v, o = views()
+    q.data = 0x100008  # not 16-byte aligned
+    assert fwd(lib, dims(), q, k, v, o) == STRIDE
+    q, k, v, o = views()
+    q.stride_t = 100  # 200-byte rows: row starts not 16-byte aligned
+    assert fwd(lib, dims(), q, k, v, o) == STRIDE
+    q, k, v, o = views()
+    v.stride_h = -192
+    assert fwd(lib, dims(), q, k, v, o) == STRIDE
+    q, k, v, o = views()
+    assert fwd(lib, dims(), q, k, v, o, S0=0x500004) == STRIDE
+
+
+def test_fwd_alias(lib):
+    q, k, v, o = views()
+    o.data = q.data
+    assert fwd(lib, dims(), q, k, v, o) == ALIAS
+    q, k, v, o = views()
+    assert fwd(lib, dims(), q, k, v, o, S0=0x500000, ST=0x500000) == ALIAS
+    q, k, v, o = views()
+    assert fwd(lib, dims(), q, k, v, o, ST=v.data) == ALIAS
+
+
+def test_workspace_queries(lib):
+    d = dims()
+    assert lib.gla_chunk_fwd_workspace(ctypes.byref(d)) >= 0
+    assert lib.gla_chunk_bwd_workspace(ctypes.byref(d)) >= 0
+    assert lib.gla_chunk_fwd_workspace(None) == 0
+    assert lib.gla_chunk_fwd_workspace(ctypes.byref(dims(B=0))) == 0
+
+
+def bwd(lib, d, q, k, v, dO, dq, dk, dv, lam=0x9000, S0=None, dST=None, dS0=None):
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    return lib.gla_chunk_bwd(ref(d), ref(q), ref(k), ref(v), lam, S0, ref(dO), dST,
+                             ref(dq), ref(dk), ref(dv), dS0, None, 0, None)
+
+
+def bwd_views():
+    q, k, v, o = views()
+    dq = T(0x600000, sb=q.stride_b, sh=q.stride_h, st=q.stride_t)
+    dk = T(0x700000, sb=q.stride_b, sh=q.stride_h, st=q.stride_t)
+    dv = T(0x800000, sb=v.stride_b, sh=v.stride_h, st=v.stride_t)
+    return q, k, v, o, dq, dk, dv
+
+
+def test_bwd_validation(lib):
+    q, k, v, dO, dq, dk, dv = bwd_views()
+    assert bwd(lib, dims(), q, k, v, None, dq, dk, dv) == NULL
+    assert bwd(lib, dims(B=0), q, k, v, dO, dq, dk, dv) == SHAPE
+    dO.dtype = gb.GLA_F32
+    assert bwd(lib, dims(), q, k, v, dO, dq, dk, dv) == DTYPE
+    q, k, v, dO, dq, dk, dv = bwd_views()
+    assert bwd(lib, dims(dk=64, dv=128), q, k, v, dO, dq, dk, dv) == UNSUP
+    q, k, v, dO, dq, dk, dv = bwd_views()
+    dk.data = dq.data
+    assert bwd(lib, dims(), q, k, v, dO, dq, dk, dv) == ALIAS
+    q, k, v, dO, dq, dk, dv = bwd_views()
+    assert bwd(lib, dims(), q, k, v, dO, dq, dk, dv, S0=0x500000, dS0=0x500000) == ALIAS
+    q, k, v, dO, dq, dk, dv = bwd_views()
+    dv.data = dO.data
+    assert bwd(lib, dims(), q, k, v, dO, dq, dk, dv) == ALIAS
+    q, k, v, dO, dq, dk, dv = bwd_views()
+    for x in (q, k, v, dO):
+        x.dtype = gb.GLA_F32
+    assert bwd(lib, dims(chunk=64), q, k, v, dO, dq, dk, dv) == UNSUP
+
+
+def dec(lib, N, H, dk, dv, q, k, v, S=0xA00000, stride=None, o=None, lam=0x9000):
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    stride = H * dk * dv if stride is None else stride
+    return lib.gla_decode_step(N, H, dk, dv, ref(q), ref(k), ref(v), lam, S, stride, ref(o), None)
+
+
+def dec_views(N=4, H=2, dk=96, dv=192):
+    q = T(0x100000, sb=H * dk, sh=dk)
+    k = T(0x200000, sb=H * dk, sh=dk)
+    v = T(0x300000, sb=H * dv, sh=dv)
+    o = T(0x400000, sb=H * dv, sh=dv)
+    return q, k, v, o
+
+
+def test_decode_validation(lib):
+    q, k, v, o = dec_views()
+    assert dec(lib, 4, 2, 96, 192, q, k, v, S=None, o=o) == NULL
+    assert dec(lib, 0, 2, 96, 192, q, k, v, o=o) == SHAPE
+    assert dec(lib, 4, 2, 64, 192, q, k, v, o=o) == UNSUP
+    assert dec(lib, 4, 2, 96, 192, q, k, v, o=o, stride=100) == SHAPE
+    assert dec(lib, 4, 2, 96, 192, q, k, v, S=0xA00004, o=o) == STRIDE
+    v.dtype = gb.GLA_F32
+    assert dec(lib, 4, 2, 96, 192, q, k, v, o=o) == DTYPE
+    q, k, v, o = dec_views()
+    o.data = q.data
+    assert dec(lib, 4, 2, 96, 192, q, k, v, o=o) == ALIAS
+    q, k, v, o = dec_views()
+    assert dec(lib, 4, 2, 96, 192, q, k, v, S=k.data, o=o) == ALIAS
