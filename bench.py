@@ -1,0 +1,304 @@
+"""Benchmark of the Simple GLA hot path on one MI355X.
+
+A step is one chunked forward + backward (gla_chunk_fwd + gla_chunk_bwd) on
+the training-shape workload: B=8, H=16, T=2048, dk=96, dv=192, chunk=128,
+bf16 q/k/v/dO, fp32 states, seeded synthetic inputs resident in HBM.  The
+JSON line's value is whole-step tokens/s (B*T per step).  The same run also
+measures the batched decode workload (1,280 sequences x 24 layers x 16 heads
+of fp32 96x192 states, 64 steps) and reports it under "decode", and times
+the fp64 CPU oracle on a bounded sample under "cpu_baseline".
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-decode] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+METRIC = "GLA fwd+bwd tokens/s (H=16,dk=96,dv=192) + decode tok/s, % roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+
+# algorithmic work per token-head (one token of one head), chunk C = 128
+C = 128
+DK, DV = 96, 192
+FWD_BYTES = 2 * (DK + DK + DV + DV)  # q, k, v in; o out (bf16)
+BWD_BYTES = 2 * (DK + DK + DV + DV) + 2 * (DK + DK + DV)  # q, k, v, dO in; dq, dk, dv out
+STATE_BYTES = DK * DV * 4
+FWD_FLOPS = 2 * C * (DK + DV) + 4 * DK * DV
+BWD_FLOPS = 2 * C * (3 * DK + 2 * DV) + 8 * DK * DV
+DEC_BYTES = 2 * STATE_BYTES + 2 * (DK + DK + DV) + 2 * DV + 4  # state r+w, q k v, o, lambda
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def event_time_ms(fn, n, stream):
+    """Average milliseconds of fn() over n calls, timed with HIP events on
+    the stream the library launches on."""
+    import torch
+
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(n):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def bench_train(gla, inputs, steps, warmup):
+    import numpy as np
+    import torch
+
+    x = inputs.make_chunk_inputs("training", with_grad=True)
+    cfg = x["cfg"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    q, k, v, dO = (d(x[n]).to(torch.bfloat16) for n in ("q", "k", "v", "dO"))
+    lam, S0 = d(x["lam"]), d(x["S0"])
+    o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv, dS0 = torch.empty_like(v), torch.empty_like(S0)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        gla.chunk_fwd(q, k, v, lam, S0, chunk=C, o=o, S_T=S_T)
+
+    def bwd():
+        gla.chunk_bwd(q, k, v, lam, dO, S0, None, chunk=C, dq=dq, dk=dk, dv=dv, dS0=dS0)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / steps
+    # per-launch durations with events (the forward is one kernel launch; the
+    # backward one call of three passes), averaged over many calls
+    n = max(10, steps)
+    ms_fwd = event_time_ms(fwd, n, stream)
+    ms_bwd = event_time_ms(bwd, n, stream)
+    units = B * H * T
+    res = dict(
+        B=B, H=H, T=T, ms_step=ms_step, ms_fwd=ms_fwd, ms_bwd=ms_bwd,
+        tokens_per_s=B * T / (ms_step / 1e3),
+        fwd_bytes=units * FWD_BYTES + 2 * B * H * STATE_BYTES,
+        bwd_bytes=units * BWD_BYTES + 2 * B * H * STATE_BYTES,
+        fwd_flops=units * FWD_FLOPS, bwd_flops=units * BWD_FLOPS,
+        lam=[float(t) for t in x["lam"]],
+    )
+    return res
+
+
+def bench_fwd_only(gla, inputs, name, reps):
+    import numpy as np
+    import torch
+
+    x = inputs.make_chunk_inputs(name)
+    cfg = x["cfg"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    q, k, v = (d(x[n]).to(torch.bfloat16) for n in ("q", "k", "v"))
+    lam = d(x["lam"])
+    S0 = d(x["S0"]) if x["S0"] is not None else None
+    o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
+    fn = lambda: gla.chunk_fwd(q, k, v, lam, S0, chunk=C, o=o, S_T=S_T)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ms = event_time_ms(fn, reps, torch.cuda.current_stream())
+    units = B * H * T
+    nbytes = units * FWD_BYTES + (2 if S0 is not None else 1) * B * H * STATE_BYTES
+    return dict(workload=name, B=B, H=H, T=T, ms=ms, tokens_per_s=B * T / (ms / 1e3),
+                gbs=nbytes / (ms / 1e3) / 1e9, hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+
+
+def bench_decode(gla, inputs, steps_override=None):
+    """1,280 sequences x 24 layers x 16 heads, fp32 states, 64 steps; each
+    step runs the 24 layer slabs in order.  Inputs for every (step, layer)
+    are drawn on the device from a seeded generator before timing."""
+    import torch
+
+    c = inputs.CONFIGS["decode"]
+    N, Lyr, H, steps = c["N"], c["L"], c["H"], steps_override or c["steps"]
+    lam = torch.tensor(inputs.lambda_log_spaced(H, 0.95, 0.9999), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5_000_001)
+    S = torch.empty((Lyr, N, H, DK, DV), dtype=torch.float32, device="cuda")
+    S.normal_(0.0, 0.01, generator=g)
+    qkv = torch.empty((steps, Lyr, N, H, DK + DK + DV), dtype=torch.bfloat16, device="cuda")
+    for st in range(steps):
+        qkv[st].copy_(torch.randn((Lyr, N, H, DK + DK + DV), generator=g, device="cuda"))
+    o = torch.empty((N, H, DV), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def run(nsteps):
+        for st in range(nsteps):
+            for layer in range(Lyr):
+                blk = qkv[st, layer]
+                gla.decode_step_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, S[layer], o=o)
+
+    # warm up on a scratch copy of one slab so the timed steps start from the seeded states
+    tmp = S[0].clone()
+    blk = qkv[0, 0]
+    for _ in range(3):
+        gla.decode_step_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, tmp, o=o)
+    del tmp
+    stream = torch.cuda.current_stream()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    run(steps)
+    e.record(stream)
+    e.synchronize()
+    ms = s.elapsed_time(e)
+    calls = steps * Lyr
+    nbytes = calls * N * H * DEC_BYTES
+    per_call_ms = ms / calls
+    return dict(
+        workload="decode: 1280 seqs x 24 layers x H=16, fp32 96x192 states, 64 steps, bf16 q/k/v",
+        N=N, layers=Lyr, H=H, steps=steps, ms_total=ms, ms_per_layer_call=per_call_ms,
+        tokens_per_s=N * steps / (ms / 1e3), gbs=nbytes / (ms / 1e3) / 1e9,
+        hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        state_gb=S.numel() * 4 / 1e9,
+    )
+
+
+def cpu_baseline(inputs):
+    """The fp64 oracle (token recurrence forward + two-sweep backward) on a
+    bounded sample of the training workload: batch entry 0 of the recipe
+    (16 heads x 2,048 tokens), timed on the host cores."""
+    import oracle
+
+    x = inputs.make_chunk_inputs("training", B=1, with_grad=True)
+    t0 = time.perf_counter()
+    oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"])
+    dt = time.perf_counter() - t0
+    T = x["cfg"]["T"]
+    return dict(value=T / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample="fwd+bwd of batch entry 0 of the training recipe (16 heads x 2048 "
+                       f"tokens), {dt:.2f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the hot path shards over (b, h) and sequences with no communication, see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_linear_attention_gla_amd import _binding as gla, inputs
+
+    gla.load_library()
+    torch.cuda.set_device(0)
+    log("bench: training-shape fwd+bwd")
+    tr = bench_train(gla, inputs, args.steps, args.warmup)
+    log(f"  step {tr['ms_step']:.3f} ms  fwd {tr['ms_fwd']:.3f} ms  bwd {tr['ms_bwd']:.3f} ms")
+    extra = {}
+    for name, reps in (("laplace", 50), ("long", 5)):
+        log(f"bench: {name} fwd")
+        extra[name + "_fwd"] = bench_fwd_only(gla, inputs, name, reps)
+        log(f"  {extra[name + '_fwd']['ms']:.3f} ms")
+    dec = None
+    if not args.no_decode:
+        log("bench: decode")
+        dec = bench_decode(gla, inputs, args.decode_steps)
+        log(f"  {dec['ms_total']:.1f} ms  {dec['gbs']:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu:
+        log("bench: cpu oracle baseline")
+        cpu = cpu_baseline(inputs)
+        log(f"  {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    # dominant kernel: the longer of the forward launch and the backward call
+    fwd_gbs = tr["fwd_bytes"] / (tr["ms_fwd"] / 1e3) / 1e9
+    bwd_gbs = tr["bwd_bytes"] / (tr["ms_bwd"] / 1e3) / 1e9
+    if tr["ms_bwd"] >= tr["ms_fwd"]:
+        dom = dict(kernel="gla_chunk_bwd (dq, dv, dk passes)", achieved=bwd_gbs,
+                   bytes_per_launch=tr["bwd_bytes"], ms_per_launch=tr["ms_bwd"])
+    else:
+        dom = dict(kernel="gla_chunk_fwd", achieved=fwd_gbs, bytes_per_launch=tr["fwd_bytes"],
+                   ms_per_launch=tr["ms_fwd"])
+    step_bytes = tr["fwd_bytes"] + tr["bwd_bytes"]
+    step_flops = tr["fwd_flops"] + tr["bwd_flops"]
+    out = {
+        "metric": METRIC,
+        "value": tr["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": tr["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "training-shape chunked GLA fwd+bwd, B=8 H=16 T=2048 dk=96 dv=192 "
+                        "chunk=128, bf16 q/k/v/dO, fp32 state",
+            "global_batch": tr["B"], "seq_len": tr["T"], "heads": tr["H"], "dk": DK, "dv": DV,
+            "chunk": C, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom["kernel"],
+            "achieved": dom["achieved"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dom["achieved"] / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": dom["bytes_per_launch"],
+            "ms_per_launch": dom["ms_per_launch"],
+        },
+        "step_roofline": {
+            "algorithmic_bytes": step_bytes,
+            "algorithmic_flops": step_flops,
+            "hbm_frac": step_bytes / (tr["ms_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": step_flops / (tr["ms_step"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+            "attainable_frac": max(step_bytes / (HBM_PEAK_GBS * 1e9),
+                                   step_flops / (BF16_PEAK_TFLOPS * 1e12)) / (tr["ms_step"] / 1e3),
+            "fwd_gbs": fwd_gbs, "bwd_gbs": bwd_gbs,
+            "ms_fwd": tr["ms_fwd"], "ms_bwd": tr["ms_bwd"],
+        },
+        "cpu_baseline": cpu,
+        "decode": dec,
+        "extra": extra,
+        "lambda": tr["lam"],
+    }
+    if dec is not None:
+        out["decode_roofline"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": dec["hbm_frac"]}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

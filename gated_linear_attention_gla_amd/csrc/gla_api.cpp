@@ -30,15 +30,21 @@ int esize(int32_t dt) { return dt == GLA_F32 ? 4 : 2; }
 bool dtype_ok(int32_t dt) { return dt == GLA_F32 || dt == GLA_BF16; }
 
 // Row starts of a (b, h, t) view must be 16-byte aligned; strides that are
-// never stepped (size-1 dims) are not constrained.
-gla_status check_view(const gla_tensor* x, int64_t nb, int64_t nh, int64_t nt, bool need_data) {
+// never stepped (size-1 dims) are not constrained.  Along t, rows of d
+// elements must not overlap (stride_t >= d) and one chunk of rows must span
+// less than 2 GiB (the kernels address a chunk tile with 32-bit offsets).
+gla_status check_view(const gla_tensor* x, int64_t nb, int64_t nh, int64_t nt, int64_t d,
+                      int64_t chunk, bool need_data) {
   if (need_data && x->data == nullptr) return GLA_ERR_NULL;
   if (x->stride_b < 0 || x->stride_h < 0 || x->stride_t < 0) return GLA_ERR_STRIDE;
   const int64_t es = esize(x->dtype);
   if ((reinterpret_cast<uintptr_t>(x->data) & 15u) != 0) return GLA_ERR_STRIDE;
   if (nb > 1 && (x->stride_b * es) % 16 != 0) return GLA_ERR_STRIDE;
   if (nh > 1 && (x->stride_h * es) % 16 != 0) return GLA_ERR_STRIDE;
-  if (nt > 1 && (x->stride_t * es) % 16 != 0) return GLA_ERR_STRIDE;
+  if (nt > 1) {
+    if ((x->stride_t * es) % 16 != 0 || x->stride_t < d) return GLA_ERR_STRIDE;
+    if (x->stride_t > ((int64_t)1 << 31) / (es * chunk)) return GLA_ERR_STRIDE;
+  }
   return GLA_OK;
 }
 
@@ -120,10 +126,11 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_te
   if (!gla::chunk_pass_supported((int)dims->dk, (int)dims->dv, (int)dims->chunk, in_f32))
     return GLA_ERR_UNSUPPORTED;
   const bool need = T > 0;
-  if ((st = check_view(q, B, H, T, need)) != GLA_OK) return st;
-  if ((st = check_view(k, B, H, T, need)) != GLA_OK) return st;
-  if ((st = check_view(v, B, H, T, need)) != GLA_OK) return st;
-  if ((st = check_view(o, B, H, T, need)) != GLA_OK) return st;
+  const int64_t DK = dims->dk, DV = dims->dv, C = dims->chunk;
+  if ((st = check_view(q, B, H, T, DK, C, need)) != GLA_OK) return st;
+  if ((st = check_view(k, B, H, T, DK, C, need)) != GLA_OK) return st;
+  if ((st = check_view(v, B, H, T, DV, C, need)) != GLA_OK) return st;
+  if ((st = check_view(o, B, H, T, DV, C, need)) != GLA_OK) return st;
   if (!aligned16(S0) || !aligned16(S_T) || !aligned16(lambda)) return GLA_ERR_STRIDE;
   if (same(o->data, q->data) || same(o->data, k->data) || same(o->data, v->data) ||
       same(S_T, S0) || same(S_T, q->data) || same(S_T, k->data) || same(S_T, v->data) ||
@@ -157,8 +164,9 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
     return GLA_ERR_UNSUPPORTED;
   const bool need = T > 0;
   const gla_tensor* views[] = {q, k, v, dO, dq, dk, dv};
-  for (const gla_tensor* x : views)
-    if ((st = check_view(x, B, H, T, need)) != GLA_OK) return st;
+  const int64_t widths[] = {DK, DK, DV, DV, DK, DK, DV};
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_view(views[i], B, H, T, widths[i], C, need)) != GLA_OK) return st;
   if (!aligned16(S0) || !aligned16(dS_T) || !aligned16(dS0) || !aligned16(lambda)) return GLA_ERR_STRIDE;
   const void* ins[] = {q->data, k->data, v->data, dO->data, lambda, S0, dS_T};
   const void* outs[] = {dq->data, dk->data, dv->data, dS0};
@@ -197,10 +205,10 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
   if (S_stride_n < H * dk * dv) return GLA_ERR_SHAPE;
   gla_status st;
   // decode views are [N, H, d]: stride_b steps n, stride_h steps h
-  if ((st = check_view(q, N, H, 1, true)) != GLA_OK) return st;
-  if ((st = check_view(k, N, H, 1, true)) != GLA_OK) return st;
-  if ((st = check_view(v, N, H, 1, true)) != GLA_OK) return st;
-  if ((st = check_view(o, N, H, 1, true)) != GLA_OK) return st;
+  if ((st = check_view(q, N, H, 1, dk, 1, true)) != GLA_OK) return st;
+  if ((st = check_view(k, N, H, 1, dk, 1, true)) != GLA_OK) return st;
+  if ((st = check_view(v, N, H, 1, dv, 1, true)) != GLA_OK) return st;
+  if ((st = check_view(o, N, H, 1, dv, 1, true)) != GLA_OK) return st;
   if (!aligned16(S) || !aligned16(lambda) || (N > 1 && (S_stride_n * 4) % 16 != 0)) return GLA_ERR_STRIDE;
   const void* ins[] = {q->data, k->data, v->data, lambda};
   for (const void* p : ins)

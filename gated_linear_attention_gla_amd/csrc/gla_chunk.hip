@@ -22,9 +22,10 @@
 //   stage 1  P^T = K Q^T tiles (causal half only), masked in fp32 -> LDS
 //   stage 2  O = diag(row factors) Q S   (state split hi+lo as bf16)
 //   stage 3  O += P V, store O
-//   stage 4  S = lam^L S + (col factors * K)^T V  (scaled K split hi+lo)
-// The split-operand products keep the state path at fp32-level accuracy; the
-// masked P tile is rounded once to bf16 (three terms for fp32 inputs).
+//   stage 4  S = lam^L S + K^T (col factors * V)  (scaled V split hi+lo)
+// Operands that are not exact bf16 values (the masked P tile, the state, the
+// decay-scaled values) enter the MFMA as hi+lo bf16 pairs (three terms for fp32
+// inputs), which keeps every product at fp32-level accuracy.
 #include "gla_common.hpp"
 #include "gla_internal.h"
 
@@ -46,56 +47,98 @@ __device__ __forceinline__ void store_planes8(bf16_t* dst0, int plane_stride, co
     bf16x8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float r = x[e];
       __bf16 t[NT];
-      split_terms<NT>(r, t);
+      split_terms<NT>(x[e], t);
       v[e] = t[p];
     }
     *reinterpret_cast<bf16x8*>(dst0 + (size_t)p * plane_stride) = v;
   }
 }
 
-// Copies rows [0, L) of a (rows x COLS) global tile into LDS (row pitch PITCH,
-// NT planes of ROWS*PITCH elements); rows in [L, ROWS) are zero-filled, and so
-// are columns [COLS, COLSP).
+// Raw storage of 8 consecutive input elements held in registers between the
+// global load and the LDS store: one 16-byte vector for bf16 inputs, two for
+// fp32 inputs (only the NT == 3 instantiations read fp32).
+template <int NT> struct Raw8;
+template <> struct Raw8<1> { bf16x8 v; };
+template <> struct Raw8<3> { f32x4 a, b; };
+
+// A (ROWS x COLS) tile of one chunk, staged global -> registers -> LDS.
+// Thread tid owns the 8-element vectors tid, tid + NTHR, ...; since NTHR is a
+// multiple of the vectors per row, its column is fixed and its rows step by
+// RPJ.  Loads go through a buffer resource whose size ends at the last valid
+// row, so rows >= L read as zero without branches; columns in [COLS, COLSP)
+// are zero.  LDS holds NT bf16 planes with row pitch PITCH.
 template <int NT, int ROWS, int COLS, int COLSP, int PITCH, int NTHR>
-__device__ __forceinline__ void stage_tile(bf16_t* lds, const void* gsrc, int64_t row_stride, int L,
-                                           int in_f32, int tid) {
-  constexpr int VPR = COLSP / 8;  // 8-element vectors per row
-  constexpr int NVEC = ROWS * VPR;
-  constexpr int PLANE = ROWS * PITCH;
-  for (int idx = tid; idx < NVEC; idx += NTHR) {
-    const int r = idx / VPR;
-    const int c = (idx - r * VPR) * 8;
-    bf16_t* dst = lds + r * PITCH + c;
-    if (r < L && c < COLS) {
+struct TileStager {
+  static constexpr int VPR = COLSP / 8;
+  static_assert(NTHR % VPR == 0, "threads must cover whole rows");
+  static constexpr int RPJ = NTHR / VPR;  // rows advanced per step j
+  static constexpr int NPER = (ROWS + RPJ - 1) / RPJ;
+  static constexpr int PLANE = ROWS * PITCH;
+  static constexpr int ES = NT == 1 ? 2 : 4;  // input element size
+  Raw8<NT> r[NPER];
+
+  // gsrc: the tile's first row; row_stride in elements; L valid rows (>= 1)
+  __device__ __forceinline__ void load(const void* gsrc, uint32_t row_stride, int L, int tid) {
+    const int row0 = tid / VPR;
+    const int c = (tid - row0 * VPR) * 8;
+    const uint32_t nbytes = ((uint32_t)(L - 1) * row_stride + COLS) * ES;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(gsrc), (short)0, (int)nbytes, 0x00020000);
+    const uint32_t voff = ((uint32_t)row0 * row_stride + c) * ES;
+    const uint32_t jstep = (uint32_t)RPJ * row_stride * ES;
+    const bool col_ok = COLSP == COLS || c < COLS;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
       if constexpr (NT == 1) {
-        // bf16 input: raw 16-byte copy
-        const bf16_t* src = reinterpret_cast<const bf16_t*>(gsrc) + (int64_t)r * row_stride + c;
-        *reinterpret_cast<bf16x8*>(dst) = *reinterpret_cast<const bf16x8*>(src);
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+        if (col_ok) v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * jstep, 0));
+        r[j].v = v;
       } else {
-        float x[8];
-        if (in_f32) {
-          const float* src = reinterpret_cast<const float*>(gsrc) + (int64_t)r * row_stride + c;
-          const float4 a = *reinterpret_cast<const float4*>(src);
-          const float4 b = *reinterpret_cast<const float4*>(src + 4);
-          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-          x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        } else {
-          const bf16_t* src = reinterpret_cast<const bf16_t*>(gsrc) + (int64_t)r * row_stride + c;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(src[e]);
+        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+        if (col_ok) {
+          x0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * jstep, 0));
+          x1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, j * jstep, 0));
         }
-        store_planes8<NT>(dst, PLANE, x);
+        r[j].a = x0;
+        r[j].b = x1;
       }
-    } else {
-      bf16x8 z;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
-#pragma unroll
-      for (int p = 0; p < NT; ++p) *reinterpret_cast<bf16x8*>(dst + p * PLANE) = z;
     }
   }
+
+  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
+    const int row0 = tid / VPR;
+    const int c = (tid - row0 * VPR) * 8;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int row = row0 + j * RPJ;
+      if (ROWS % RPJ == 0 || row < ROWS) {
+        bf16_t* dst = lds + row * PITCH + c;
+        if constexpr (NT == 1) {
+          *reinterpret_cast<bf16x8*>(dst) = r[j].v;
+        } else {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = r[j].a[e];
+            x[4 + e] = r[j].b[e];
+          }
+          store_planes8<NT>(dst, PLANE, x);
+        }
+      }
+    }
+  }
+};
+
+// Causal P tiles in the forward enumeration: t -> (I', J') with J' <= I',
+// t = I'(I'+1)/2 + J'.  Wave-uniform scalar arithmetic.
+__device__ __forceinline__ void tile_of(int t, int& Ip, int& Jp) {
+  int i = 0;
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+  Ip = i;
+  Jp = t - i * (i + 1) / 2;
 }
 
 template <int DK, int DV, int BN, int NW, int C, int NT>
@@ -108,22 +151,33 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   constexpr int NBLK = DV / BN;
   constexpr int CP = (C + 31) / 32 * 32;    // chunk rows padded to the 32-deep k-step
   constexpr int DKP = (DK + 31) / 32 * 32;  // DK padded likewise
-  constexpr int NTP = NT == 3 ? 3 : 1;      // terms of the masked P tile
+  constexpr int NTP = NT == 3 ? 3 : 2;      // terms of the masked P tile
   constexpr int NTS = NT == 3 ? 3 : 2;      // terms of state fragments
-  constexpr int NTK = NT == 3 ? 3 : 2;      // terms of decay-scaled keys
+  constexpr int NTK = NT == 3 ? 3 : 2;      // terms of decay-scaled values
   constexpr int PQ = DKP + 8;               // LDS row pitches (elements)
-  constexpr int PVV = BN + 8;
+  constexpr int PVV = BN + 16;  // column reads of V: conflict-free at this pitch
   constexpr int PP = CP + 8;
   constexpr int DKT = DK / 16;  // 16-row tiles of the state
   constexpr int KSD = DKP / 32;  // 32-deep k-steps over DK
   constexpr int CT = CP / 16;    // 16-row tiles of a chunk
   constexpr int KSC = CP / 32;   // 32-deep k-steps over the chunk
+  constexpr int NPT = CT * (CT + 1) / 2;  // causal P tiles
+  constexpr int MAXPT = (NPT + NW - 1) / NW;
 
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[NT * CP * PQ];
+  // LDS: query, key and value tiles plus the masked P tile.  When the four do
+  // not fit, P is held in registers until every read of the query tile is
+  // done and then written over it.
+  constexpr int Q_ELEMS = NT * CP * PQ;
+  constexpr int P_ELEMS = NTP * CP * PP;
+  constexpr int SEPARATE_BYTES = 2 * (2 * Q_ELEMS + NT * CP * PVV + P_ELEMS) + 4 * (CP + 2);
+  constexpr bool ALIAS_P = SEPARATE_BYTES > 160 * 1024 - 512;
+  constexpr int QP_ELEMS = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS) : Q_ELEMS + P_ELEMS;
+  __shared__ __attribute__((aligned(16))) bf16_t sQP[QP_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t sK[NT * CP * PQ];
   __shared__ __attribute__((aligned(16))) bf16_t sV[NT * CP * PVV];
-  __shared__ __attribute__((aligned(16))) bf16_t sP[NTP * CP * PP];
   __shared__ float sPow[CP + 2];
+  bf16_t* const sQ = sQP;
+  bf16_t* const sP = ALIAS_P ? sQP : sQP + Q_ELEMS;
 
   // XCD-aware block decode: consecutive dispatch slots on one XCD (block ids
   // congruent mod 8) walk the column blocks of the same (b, h), so the q/k
@@ -139,7 +193,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   const int64_t h = bh - b * a.H;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l = tid & 63;
   const int g = l >> 4;
   const int li = l & 15;
@@ -155,11 +209,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   const int64_t q_off = b * a.sq_b + h * a.sq_h;
   const int64_t k_off = b * a.sk_b + h * a.sk_h;
   const int64_t v_off = b * a.sv_b + h * a.sv_h + (int64_t)nblk * BN;
+  const int col0 = nblk * BN + w * NS * 16 + li;  // + 16 s: this lane's column in strip s
 
-  // column of this lane inside strip s (global state/output column)
-  auto colof = [&](int s) { return nblk * BN + (w * NS + s) * 16 + li; };
-
-  // ---- state slice in accumulators: accS[D][s][r] = S[16 D + 4 g + r][colof(s)]
+  // ---- state slice in accumulators: accS[D][s][r] = S[16 D + 4 g + r][col0 + 16 s]
   f32x4 accS[DKT][NS];
   {
     const float* si = a.s_init ? a.s_init + bh * (int64_t)DK * DV : nullptr;
@@ -170,101 +222,153 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int d = 16 * D + 4 * g + r;
-          const int n = colof(s);
+          const int n = col0 + 16 * s;
           float x = 0.0f;
           if (si) x = a.s_init_trans ? si[(int64_t)n * DK + d] : si[(int64_t)d * DV + n];
           accS[D][s][r] = x;
         }
   }
 
+  // writes 4 consecutive masked-P values of row i (cols 16 J + 4 g ..) as NTP planes
+  auto put_p = [&](int i, int J, const f32x4& val) {
+#pragma unroll
+    for (int p = 0; p < NTP; ++p) {
+      bf16x4 pk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __bf16 t[NTP];
+        split_terms<NTP>(val[r], t);
+        pk[r] = t[p];
+      }
+      *reinterpret_cast<bf16x4*>(&sP[p * CP * PP + i * PP + 16 * J + 4 * g]) = pk;
+    }
+  };
+  // zero tiles read by the 32-deep k-steps of stage 3: forward (I, I+1) for
+  // even I, reverse (I, I-1) for odd I
+  auto put_zero_tiles = [&]() {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int zi = w; zi < CT / 2; zi += NW) {
+      const int I = rev ? 2 * zi + 1 : 2 * zi;
+      put_p(16 * I + li, rev ? I - 1 : I + 1, z);
+    }
+  };
+
   const int64_t T = a.T;
   const int64_t nchunks = (T + C - 1) / C;
+  // chunk ci of the walk (reverse time walks the chunks backwards)
+  auto chunk_start = [&](int64_t ci) { return (rev ? (nchunks - 1 - ci) : ci) * C; };
+  auto chunk_len = [&](int64_t t0) { return (int)((T - t0) < C ? (T - t0) : C); };
+
+  // The next chunk's tiles are loaded into registers while the current chunk
+  // is computed, so HBM latency overlaps the MFMA work.
+  TileStager<NT, CP, DK, DKP, PQ, NTHR> pfq, pfk;
+  TileStager<NT, CP, BN, BN, PVV, NTHR> pfv;
+  // With wide query/key rows the three prefetched tiles do not fit in
+  // registers next to the state; the query tile is then fetched later in the
+  // chunk, once the P tile has left the registers.
+  constexpr bool LATE_Q = DK > 128;
+  auto prefetch_q = [&](int64_t ci) {
+    const int64_t t0 = chunk_start(ci);
+    pfq.load(qb + (q_off + t0 * a.sq_t) * esz, (uint32_t)a.sq_t, chunk_len(t0), tid);
+  };
+  auto prefetch_kv = [&](int64_t ci) {
+    const int64_t t0 = chunk_start(ci);
+    const int Ln = chunk_len(t0);
+    pfk.load(kb + (k_off + t0 * a.sk_t) * esz, (uint32_t)a.sk_t, Ln, tid);
+    pfv.load(vb + (v_off + t0 * a.sv_t) * esz, (uint32_t)a.sv_t, Ln, tid);
+  };
+  if (nchunks > 0) {
+    prefetch_q(0);
+    prefetch_kv(0);
+  }
+
   for (int64_t ci = 0; ci < nchunks; ++ci) {
-    const int64_t c = rev ? (nchunks - 1 - ci) : ci;
-    const int64_t t0 = c * C;
-    const int L = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t t0 = chunk_start(ci);
+    const int L = chunk_len(t0);
 
-    // ---------------- stage 0: tiles -> LDS
-    stage_tile<NT, CP, DK, DKP, PQ, NTHR>(sQ, qb + (q_off + t0 * a.sq_t) * esz, a.sq_t, L, a.in_f32, tid);
-    stage_tile<NT, CP, DK, DKP, PQ, NTHR>(sK, kb + (k_off + t0 * a.sk_t) * esz, a.sk_t, L, a.in_f32, tid);
-    stage_tile<NT, CP, BN, BN, PVV, NTHR>(sV, vb + (v_off + t0 * a.sv_t) * esz, a.sv_t, L, a.in_f32, tid);
+    // ---------------- stage 0: prefetched tiles -> LDS, start the next loads
+    pfq.store(sQ, tid);
+    pfk.store(sK, tid);
+    pfv.store(sV, tid);
     __syncthreads();
-
-    // ---------------- stage 1: masked P tiles (P[i][j] stored row-major)
-    {
-      int idx = 0;
-#pragma unroll
-      for (int I = 0; I < CT; ++I) {
-#pragma unroll
-        for (int J = 0; J < CT; ++J) {
-          const bool need = rev ? (J >= I) : (J <= I);
-          const bool zero = rev ? (J == I - 1 && (I & 1)) : (J == I + 1 && !(I & 1));
-          if (!need && !zero) continue;
-          if ((idx++ % NW) != w) continue;
-          const int i = 16 * I + li;
-          if (need) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-              bf16x8 A[NT], Bq[NT];
-#pragma unroll
-              for (int p = 0; p < NT; ++p) {
-                A[p] = lds_read_b128(&sK[p * CP * PQ + (16 * J + li) * PQ + 32 * ks + 8 * g]);
-                Bq[p] = lds_read_b128(&sQ[p * CP * PQ + i * PQ + 32 * ks + 8 * g]);
-              }
-              mma_split<NT, NT>(acc, A, Bq);
-            }
-            // acc[r] = q'_i . k'_j with j = 16 J + 4 g + r
-            float val[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = 16 * J + 4 * g + r;
-              const int diff = rev ? (j - i) : (i - j);
-              val[r] = diff >= 0 ? acc[r] * sPow[diff] : 0.0f;
-            }
-#pragma unroll
-            for (int p = 0; p < NTP; ++p) {
-              bf16x4 pk;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                __bf16 t[NTP];
-                split_terms<NTP>(val[r], t);
-                pk[r] = t[p];
-              }
-              *reinterpret_cast<bf16x4*>(&sP[p * CP * PP + i * PP + 16 * J + 4 * g]) = pk;
-            }
-          } else {
-            bf16x4 z;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) z[r] = (__bf16)0.0f;
-#pragma unroll
-            for (int p = 0; p < NTP; ++p)
-              *reinterpret_cast<bf16x4*>(&sP[p * CP * PP + i * PP + 16 * J + 4 * g]) = z;
-          }
-        }
-      }
+    if (ci + 1 < nchunks) {
+      if constexpr (!LATE_Q) prefetch_q(ci + 1);
+      prefetch_kv(ci + 1);
     }
+
+    // ---------------- stage 1: masked P tiles (causal half), P[i][j] row-major
+    f32x4 ptile[ALIAS_P ? MAXPT : 1];
+#pragma unroll
+    for (int kt = 0; kt < MAXPT; ++kt) {
+      const int t = w + kt * NW;
+      if (t < NPT) {
+        int Ip, Jp;
+        tile_of(t, Ip, Jp);
+        const int I = rev ? CT - 1 - Ip : Ip;
+        const int J = rev ? CT - 1 - Jp : Jp;
+        const int i = 16 * I + li;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          bf16x8 A[NT], Bq[NT];
+#pragma unroll
+          for (int p = 0; p < NT; ++p) {
+            A[p] = lds_read_b128(&sK[p * CP * PQ + (16 * J + li) * PQ + 32 * ks + 8 * g]);
+            Bq[p] = lds_read_b128(&sQ[p * CP * PQ + i * PQ + 32 * ks + 8 * g]);
+          }
+          mma_split<NT, NT>(acc, A, Bq);
+        }
+        // acc[r] = q'_i . k'_j with j = 16 J + 4 g + r; apply the decay mask
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * J + 4 * g + r;
+          const int diff = rev ? (j - i) : (i - j);
+          acc[r] = diff >= 0 ? acc[r] * sPow[diff] : 0.0f;
+        }
+        if constexpr (ALIAS_P) ptile[kt] = acc;
+        else put_p(i, J, acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!ALIAS_P) put_zero_tiles();
 
     // ---------------- stage 2: O = diag(row factors) Q S
     f32x4 accO[CT][NS];
-    {
+#pragma unroll
+    for (int I = 0; I < CT; ++I)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) accO[I][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
       // State as the B operand of Q S: k-slot e of lane group g holds state
       // row 32 ks + 16 (e / 4) + 4 g + (e % 4), which is what the accumulator
       // layout already gives this lane; Q is read with the same permutation.
-      bf16x8 Sf[KSD][NS][NTS];
+      bf16x8 Sf[NS][NTS];
 #pragma unroll
-      for (int ks = 0; ks < KSD; ++ks)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int e = 0; e < 8; ++e) {
+          const int D = 2 * ks + (e >> 2);
+          const float x = (D < DKT) ? accS[D < DKT ? D : 0][s][e & 3] : 0.0f;
+          __bf16 t[NTS];
+          split_terms<NTS>(x, t);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int D = 2 * ks + (e >> 2);
-            const float x = (D < DKT) ? accS[D < DKT ? D : 0][s][e & 3] : 0.0f;
-            __bf16 t[NTS];
-            split_terms<NTS>(x, t);
+          for (int p = 0; p < NTS; ++p) Sf[s][p][e] = t[p];
+        }
 #pragma unroll
-            for (int p = 0; p < NTS; ++p) Sf[ks][s][p][e] = t[p];
-          }
+      for (int I = 0; I < CT; ++I) {
+        bf16x8 Aq[NT];
+#pragma unroll
+        for (int p = 0; p < NT; ++p) {
+          const bf16_t* row = &sQ[p * CP * PQ + (16 * I + li) * PQ + 32 * ks];
+          Aq[p] = cat4(lds_read_b64(row + 4 * g), lds_read_b64(row + 16 + 4 * g));
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) mma_split<NT, NTS>(accO[I][s], Aq, Sf[s]);
+        if (I % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {
       const float cfac = sPow[L];
 #pragma unroll
       for (int D = 0; D < DKT; ++D)
@@ -272,22 +376,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         for (int s = 0; s < NS; ++s)
 #pragma unroll
           for (int r = 0; r < 4; ++r) accS[D][s][r] *= cfac;
-
 #pragma unroll
-      for (int I = 0; I < CT; ++I) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) accO[I][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          bf16x8 Aq[NT];
-#pragma unroll
-          for (int p = 0; p < NT; ++p) {
-            const bf16_t* row = &sQ[p * CP * PQ + (16 * I + li) * PQ + 32 * ks];
-            Aq[p] = cat4(lds_read_b64(row + 4 * g), lds_read_b64(row + 16 + 4 * g));
-          }
-#pragma unroll
-          for (int s = 0; s < NS; ++s) mma_split<NT, NTS>(accO[I][s], Aq, Sf[ks][s]);
-        }
+      for (int I = 0; I < CT; ++I)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * I + 4 * g + r;
@@ -295,12 +385,30 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
           for (int s = 0; s < NS; ++s) accO[I][s][r] *= f;
         }
+    }
+
+    if constexpr (ALIAS_P) {
+      __syncthreads();  // every read of the query tile is done
+#pragma unroll
+      for (int kt = 0; kt < MAXPT; ++kt) {
+        const int t = w + kt * NW;
+        if (t < NPT) {
+          int Ip, Jp;
+          tile_of(t, Ip, Jp);
+          const int I = rev ? CT - 1 - Ip : Ip;
+          const int J = rev ? CT - 1 - Jp : Jp;
+          put_p(16 * I + li, J, ptile[kt]);
+        }
       }
+      put_zero_tiles();
     }
     __syncthreads();  // P complete
+    if constexpr (LATE_Q) {
+      if (ci + 1 < nchunks) prefetch_q(ci + 1);
+    }
 
     // ---------------- stage 3: O += P V ; stage 4: S += (colfac K)^T V
-#pragma unroll
+#pragma unroll 1
     for (int ks = 0; ks < KSC; ++ks) {
       // V fragments: B[k = 32 ks + 8 g + e][n = strip col + li] via column reads
       bf16x8 Bv[NS][NT];
@@ -324,57 +432,76 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
           Ap[p] = lds_read_b128(&sP[p * CP * PP + (16 * I + li) * PP + 32 * ks + 8 * g]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma_split<NTP, NT>(accO[I][s], Ap, Bv[s]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // stage 4: decay-scaled keys as the A operand, A[m = d][k = j]
-      float cf[8];
+      // stage 4: S += K^T (diag(col factors) V).  The decay rides on this
+      // wave's own value strip (split hi/lo); the keys enter exact.
+      bf16x8 Bs[NS][NTK];
+      {
+        float cf[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 32 * ks + 8 * g + e;
-        cf[e] = (j < L) ? (rev ? sPow[j + 1] : sPow[L - 1 - j]) : 0.0f;
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * ks + 8 * g + e;
+          cf[e] = (j < L) ? (rev ? sPow[j + 1] : sPow[L - 1 - j]) : 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float x = 0.0f;
+#pragma unroll
+            for (int p = 0; p < NT; ++p) x += bf16v_to_f32(Bv[s][p][e]);
+            __bf16 t[NTK];
+            split_terms<NTK>(x * cf[e], t);
+#pragma unroll
+            for (int p = 0; p < NTK; ++p) Bs[s][p][e] = t[p];
+          }
       }
 #pragma unroll
       for (int D = 0; D < DKT; ++D) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        // keys as the A operand, A[m = d][k = j], via column reads
+        bf16x8 Ak[NT];
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
           const bf16_t* base = &sK[p * CP * PQ + (32 * ks + 8 * g + (li >> 2)) * PQ + 16 * D + 4 * (li & 3)];
-          const bf16x8 raw = cat4(lds_read_tr(base), lds_read_tr(base + 4 * PQ));
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] += bf16v_to_f32(raw[e]);
-        }
-        bf16x8 Ak[NTK];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          __bf16 t[NTK];
-          split_terms<NTK>(x[e] * cf[e], t);
-#pragma unroll
-          for (int p = 0; p < NTK; ++p) Ak[p][e] = t[p];
+          Ak[p] = cat4(lds_read_tr(base), lds_read_tr(base + 4 * PQ));
         }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) mma_split<NTK, NT>(accS[D][s], Ak, Bv[s]);
+        for (int s = 0; s < NS; ++s) mma_split<NT, NTK>(accS[D][s], Ak, Bs[s]);
+        // keep the scheduler from hoisting every row tile's loads at once
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // store O rows < L
+    // store O rows < L: the buffer resource ends at the last valid row, so
+    // stores of rows >= L are dropped by the hardware range check.  The lane
+    // part of the offset is a VGPR, the row/strip part a uniform SGPR.
     {
-      char* ob = reinterpret_cast<char*>(a.o);
+      const int oes = a.o_f32 ? 4 : 2;
+      char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + t0 * a.so_t) * oes;
+      const uint32_t so_t = (uint32_t)a.so_t;
+      const uint32_t nbytes = ((uint32_t)(L - 1) * so_t + DV) * oes;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)nbytes, 0x00020000);
+      const uint32_t lane_off = ((uint32_t)(4 * g) * so_t + col0) * oes;
+      if (a.o_f32) {
 #pragma unroll
-      for (int I = 0; I < CT; ++I)
+        for (int I = 0; I < CT; ++I)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + 4 * g + r;
-          if (i < L) {
-            const int64_t rowoff = b * a.so_b + h * a.so_h + (t0 + i) * a.so_t;
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const int64_t off = rowoff + colof(s);
-              if (a.o_f32) reinterpret_cast<float*>(ob)[off] = accO[I][s][r];
-              else reinterpret_cast<bf16_t*>(ob)[off] = f32_to_bf16(accO[I][s][r]);
-            }
-          }
-        }
+            for (int s = 0; s < NS; ++s)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(accO[I][s][r]), rs, lane_off,
+                                                    (int)(((16 * I + r) * so_t + 16 * s) * 4), 0);
+      } else {
+#pragma unroll
+        for (int I = 0; I < CT; ++I)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(accO[I][s][r]), rs, lane_off,
+                                                    (int)(((16 * I + r) * so_t + 16 * s) * 2), 0);
+      }
     }
     __syncthreads();  // LDS reuse by the next chunk
   }
@@ -386,7 +513,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sf[(int64_t)(16 * D + 4 * g + r) * DV + colof(s)] = accS[D][s][r];
+        for (int r = 0; r < 4; ++r) sf[(int64_t)(16 * D + 4 * g + r) * DV + col0 + 16 * s] = accS[D][s][r];
   }
 }
 
@@ -405,7 +532,7 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
 template <int DK, int DV, int C, int NT>
 static hipError_t launch_shape(const ChunkArgs& a, hipStream_t st) {
   if constexpr (DK == 96 && DV == 192) return launch_one<96, 192, 96, 6, C, NT>(a, st);
-  else if constexpr (DK == 192 && DV == 96) return launch_one<192, 96, 48, 3, C, NT>(a, st);
+  else if constexpr (DK == 192 && DV == 96) return launch_one<192, 96, 96, 6, C, NT>(a, st);
   else if constexpr (DK == 16 && DV == 32) return launch_one<16, 32, 32, 2, C, NT>(a, st);
   else if constexpr (DK == 32 && DV == 16) return launch_one<32, 16, 16, 1, C, NT>(a, st);
   else return hipErrorInvalidValue;

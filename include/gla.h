@@ -35,7 +35,9 @@
  *               (b, h, t, d) lives at data + (b*stride_b + h*stride_h +
  *               t*stride_t + d) elements; d is contiguous.  Strides are in
  *               elements, non-negative.  The base pointer and every row start
- *               must be 16-byte aligned (GLA_ERR_STRIDE otherwise).  Both the
+ *               must be 16-byte aligned; rows along t must not overlap
+ *               (stride_t >= d) and stride_t * element size * chunk must be
+ *               below 2^31 bytes (GLA_ERR_STRIDE otherwise).  Both the
  *               head-major [B,H,T,d] and the token-major [B,T,H,d] layouts
  *               are accepted without copies.
  *   Dtypes      q, k, v (and dO) share one dtype, GLA_BF16 or GLA_F32.
