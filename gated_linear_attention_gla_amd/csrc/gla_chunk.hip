@@ -20,12 +20,14 @@
 // in MFMA accumulators.  Each wave owns NS strips of 16 columns.  Per chunk:
 //   stage 0  q, k, v tiles -> LDS (bf16 planes; fp32 inputs become 3 planes)
 //   stage 1  P^T = K Q^T tiles (causal half only), masked in fp32 -> LDS
-//   stage 2  O = diag(row factors) Q S   (state split hi+lo as bf16)
-//   stage 3  O += P V, store O
+//   stage 2  O^T = S^T Q^T, scaled by the row factors (state split hi+lo)
+//   stage 3  O^T += V^T P^T, store O (O^T tiles give each lane 4 adjacent columns)
 //   stage 4  S = lam^L S + K^T (col factors * V)  (scaled V split hi+lo)
 // Operands that are not exact bf16 values (the masked P tile, the state, the
 // decay-scaled values) enter the MFMA as hi+lo bf16 pairs (three terms for fp32
 // inputs), which keeps every product at fp32-level accuracy.
+#include <type_traits>
+
 #include "gla_common.hpp"
 #include "gla_internal.h"
 
@@ -171,13 +173,26 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   constexpr int P_ELEMS = NTP * CP * PP;
   constexpr int SEPARATE_BYTES = 2 * (2 * Q_ELEMS + NT * CP * PVV + P_ELEMS) + 4 * (CP + 2);
   constexpr bool ALIAS_P = SEPARATE_BYTES > 160 * 1024 - 512;
-  constexpr int QP_ELEMS = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS) : Q_ELEMS + P_ELEMS;
+  // output staging (see the store stage): CP rows of BN values at pitch OP2
+  // (bf16) or OP4 (fp32)
+  constexpr int OP2 = BN + 8;
+  constexpr int OP4 = BN + 4;
+  constexpr int STG_ELEMS = CP * OP4 * 2;  // bf16 units, fp32 case (the larger)
+  constexpr int QP_RAW = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS) : Q_ELEMS + P_ELEMS;
+  constexpr int QP_ELEMS = QP_RAW > STG_ELEMS ? QP_RAW : STG_ELEMS;
+  constexpr bool STG_IN_P = !ALIAS_P && STG_ELEMS <= P_ELEMS;
   __shared__ __attribute__((aligned(16))) bf16_t sQP[QP_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t sK[NT * CP * PQ];
   __shared__ __attribute__((aligned(16))) bf16_t sV[NT * CP * PVV];
   __shared__ float sPow[CP + 2];
+  // per-chunk factor tables for a chunk of L tokens: row factors (how the
+  // entry state reaches row i) and column factors (how row j's key/value pair
+  // reaches the exit state); zero beyond L
+  __shared__ __attribute__((aligned(16))) float sRowF[CP];
+  __shared__ __attribute__((aligned(16))) float sColF[CP];
   bf16_t* const sQ = sQP;
   bf16_t* const sP = ALIAS_P ? sQP : sQP + Q_ELEMS;
+
 
   // XCD-aware block decode: consecutive dispatch slots on one XCD (block ids
   // congruent mod 8) walk the column blocks of the same (b, h), so the q/k
@@ -201,6 +216,23 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 
   const float lam = a.lam[h];
   for (int n = tid; n <= CP + 1; n += NTHR) sPow[n] = lam_pow_f32(lam, n);
+  auto fill_factors = [&](int Lc) {
+    for (int n = tid; n < CP; n += NTHR) {
+      const bool in = n < Lc;
+      const int er = rev ? Lc - 1 - n : n + 1;  // row exponent
+      const int ec = rev ? n + 1 : Lc - 1 - n;  // column exponent
+      sRowF[n] = in ? lam_pow_f32(lam, er) : 0.0f;
+      sColF[n] = in ? lam_pow_f32(lam, ec) : 0.0f;
+    }
+  };
+  // decay mask of the diagonal P tiles, per lane: forward keeps j <= i with
+  // lam^(i-j), reverse keeps j >= i with lam^(j-i); i = 16 I + li, j = 16 I + 4 g + r
+  float dmask[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = rev ? (4 * g + r - li) : (li - 4 * g - r);
+    dmask[r] = d >= 0 ? lam_pow_f32(lam, d) : 0.0f;
+  }
 
   const char* qb = reinterpret_cast<const char*>(a.q);
   const char* kb = reinterpret_cast<const char*>(a.k);
@@ -264,8 +296,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   TileStager<NT, CP, DK, DKP, PQ, NTHR> pfq, pfk;
   TileStager<NT, CP, BN, BN, PVV, NTHR> pfv;
   // With wide query/key rows the three prefetched tiles do not fit in
-  // registers next to the state; the query tile is then fetched later in the
-  // chunk, once the P tile has left the registers.
+  // registers next to the state and the P tile; the next query tile is then
+  // fetched only after stage 4, while the output is staged and stored.
   constexpr bool LATE_Q = DK > 128;
   auto prefetch_q = [&](int64_t ci) {
     const int64_t t0 = chunk_start(ci);
@@ -277,19 +309,24 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     pfk.load(kb + (k_off + t0 * a.sk_t) * esz, (uint32_t)a.sk_t, Ln, tid);
     pfv.load(vb + (v_off + t0 * a.sv_t) * esz, (uint32_t)a.sv_t, Ln, tid);
   };
+  // Chunk pipeline.  The tiles of chunk ci+1 are loaded into registers while
+  // chunk ci is computed and written to LDS as soon as its last reader is
+  // done; the output of chunk ci is stored last, so its write latency
+  // overlaps the compute of chunk ci+1.
   if (nchunks > 0) {
     prefetch_q(0);
     prefetch_kv(0);
+    pfq.store(sQ, tid);
+    pfk.store(sK, tid);
+    pfv.store(sV, tid);
+    fill_factors(chunk_len(chunk_start(0)));
   }
 
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = chunk_start(ci);
     const int L = chunk_len(t0);
 
-    // ---------------- stage 0: prefetched tiles -> LDS, start the next loads
-    pfq.store(sQ, tid);
-    pfk.store(sK, tid);
-    pfv.store(sV, tid);
+    // ---------------- stage 0: this chunk's tiles are in LDS; start the next loads
     __syncthreads();
     if (ci + 1 < nchunks) {
       if constexpr (!LATE_Q) prefetch_q(ci + 1);
@@ -318,12 +355,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
           }
           mma_split<NT, NT>(acc, A, Bq);
         }
-        // acc[r] = q'_i . k'_j with j = 16 J + 4 g + r; apply the decay mask
+        // acc[r] = q'_i . k'_j with j = 16 J + 4 g + r; apply the decay mask.
+        // Off the diagonal every entry is inside the causal window and the
+        // exponent is 16 (Ip - Jp) + base -/+ r.
+        if (Ip == Jp) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * J + 4 * g + r;
-          const int diff = rev ? (j - i) : (i - j);
-          acc[r] = diff >= 0 ? acc[r] * sPow[diff] : 0.0f;
+          for (int r = 0; r < 4; ++r) acc[r] *= dmask[r];
+        } else {
+          const int base = 16 * (Ip - Jp) + (rev ? 4 * g - li : li - 4 * g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] *= sPow[rev ? base + r : base - r];
         }
         if constexpr (ALIAS_P) ptile[kt] = acc;
         else put_p(i, J, acc);
@@ -332,7 +373,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     }
     if constexpr (!ALIAS_P) put_zero_tiles();
 
-    // ---------------- stage 2: O = diag(row factors) Q S
+    // ---------------- stage 2: O^T = S^T Q^T, rows scaled by the row factors
     f32x4 accO[CT][NS];
 #pragma unroll
     for (int I = 0; I < CT; ++I)
@@ -364,7 +405,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
           Aq[p] = cat4(lds_read_b64(row + 4 * g), lds_read_b64(row + 16 + 4 * g));
         }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) mma_split<NT, NTS>(accO[I][s], Aq, Sf[s]);
+        for (int s = 0; s < NS; ++s) mma_split<NTS, NT>(accO[I][s], Sf[s], Aq);
         if (I % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -377,14 +418,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) accS[D][s][r] *= cfac;
 #pragma unroll
-      for (int I = 0; I < CT; ++I)
+      for (int I = 0; I < CT; ++I) {
+        const int i = 16 * I + li;
+        const float f = sRowF[i];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + 4 * g + r;
-          const float f = rev ? (i < L ? sPow[L - 1 - i] : 0.0f) : sPow[i + 1];
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int s = 0; s < NS; ++s) accO[I][s][r] *= f;
-        }
+          for (int r = 0; r < 4; ++r) accO[I][s][r] *= f;
+      }
     }
 
     if constexpr (ALIAS_P) {
@@ -403,9 +444,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
       put_zero_tiles();
     }
     __syncthreads();  // P complete
-    if constexpr (LATE_Q) {
-      if (ci + 1 < nchunks) prefetch_q(ci + 1);
-    }
 
     // ---------------- stage 3: O += P V ; stage 4: S += (colfac K)^T V
 #pragma unroll 1
@@ -431,19 +469,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         for (int p = 0; p < NTP; ++p)
           Ap[p] = lds_read_b128(&sP[p * CP * PP + (16 * I + li) * PP + 32 * ks + 8 * g]);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) mma_split<NTP, NT>(accO[I][s], Ap, Bv[s]);
+        for (int s = 0; s < NS; ++s) mma_split<NT, NTP>(accO[I][s], Bv[s], Ap);
         __builtin_amdgcn_sched_barrier(0);
       }
       // stage 4: S += K^T (diag(col factors) V).  The decay rides on this
       // wave's own value strip (split hi/lo); the keys enter exact.
       bf16x8 Bs[NS][NTK];
       {
-        float cf[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 32 * ks + 8 * g + e;
-          cf[e] = (j < L) ? (rev ? sPow[j + 1] : sPow[L - 1 - j]) : 0.0f;
-        }
+        const f32x4 cf0 = *reinterpret_cast<const f32x4*>(&sColF[32 * ks + 8 * g]);
+        const f32x4 cf1 = *reinterpret_cast<const f32x4*>(&sColF[32 * ks + 8 * g + 4]);
+        const float cf[8] = {cf0[0], cf0[1], cf0[2], cf0[3], cf1[0], cf1[1], cf1[2], cf1[3]};
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -473,37 +508,87 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
       }
     }
 
-    // store O rows < L: the buffer resource ends at the last valid row, so
-    // stores of rows >= L are dropped by the hardware range check.  The lane
-    // part of the offset is a VGPR, the row/strip part a uniform SGPR.
+    // ---------------- next chunk's tiles -> LDS; store O (rows < L)
+    // O is staged through LDS so that the global stores are 16-byte,
+    // row-contiguous and coalesced.  accO holds O^T tiles: lane (g, li) has
+    // row 16 I + li, columns strip + 4 g .. + 3.  The staging buffer is the P
+    // region when it fits, else the query+P region (then the next chunk's
+    // tiles are written only after the staged output has been read).  The
+    // buffer resource ends at the last valid row, so stores of rows >= L are
+    // dropped by the hardware range check.
+    __syncthreads();  // every wave is done with the P, key and value tiles
+    const bool more = ci + 1 < nchunks;
+    if constexpr (LATE_Q) {
+      if (more) prefetch_q(ci + 1);
+    }
+    // the factor tables change only when the next chunk's length differs
+    const bool refill = more && chunk_len(chunk_start(ci + 1)) != L;
+    if constexpr (STG_IN_P) {
+      if (more) {
+        pfq.store(sQ, tid);
+        pfk.store(sK, tid);
+        pfv.store(sV, tid);
+      }
+      if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
+    }
     {
-      const int oes = a.o_f32 ? 4 : 2;
-      char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + t0 * a.so_t) * oes;
-      const uint32_t so_t = (uint32_t)a.so_t;
-      const uint32_t nbytes = ((uint32_t)(L - 1) * so_t + DV) * oes;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)nbytes, 0x00020000);
-      const uint32_t lane_off = ((uint32_t)(4 * g) * so_t + col0) * oes;
-      if (a.o_f32) {
+      const int f32o = a.o_f32;
+      bf16_t* stg = STG_IN_P ? sP : sQP;
+      if (f32o) {
+        float* st4 = reinterpret_cast<float*>(stg);
 #pragma unroll
         for (int I = 0; I < CT; ++I)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(accO[I][s][r]), rs, lane_off,
-                                                    (int)(((16 * I + r) * so_t + 16 * s) * 4), 0);
+          for (int s = 0; s < NS; ++s)
+            *reinterpret_cast<f32x4*>(&st4[(16 * I + li) * OP4 + (w * NS + s) * 16 + 4 * g]) = accO[I][s];
       } else {
 #pragma unroll
         for (int I = 0; I < CT; ++I)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+          for (int s = 0; s < NS; ++s) {
+            bf16x4 pk;
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(accO[I][s][r]), rs, lane_off,
-                                                    (int)(((16 * I + r) * so_t + 16 * s) * 2), 0);
+            for (int r = 0; r < 4; ++r) pk[r] = (__bf16)accO[I][s][r];
+            *reinterpret_cast<bf16x4*>(&stg[(16 * I + li) * OP2 + (w * NS + s) * 16 + 4 * g]) = pk;
+          }
       }
+      __syncthreads();
+      const int oes = f32o ? 4 : 2;
+      char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + t0 * a.so_t + nblk * BN) * oes;
+      const uint32_t so_t = (uint32_t)a.so_t;
+      const uint32_t nbytes = ((uint32_t)(L - 1) * so_t + BN) * oes;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)nbytes, 0x00020000);
+      // thread tid stores column vector tid % VPR of rows tid / VPR + RPJ j
+      auto store_rows = [&](auto vpr_c, auto es_c) {
+        constexpr int VPR = decltype(vpr_c)::value;  // 16-byte vectors per row
+        constexpr int ES = decltype(es_c)::value;
+        static_assert(NTHR % VPR == 0, "threads must cover whole rows");
+        constexpr int RPJ = NTHR / VPR;
+        constexpr int PITCH_B = ES == 4 ? OP4 * 4 : OP2 * 2;  // staging pitch in bytes
+        const int row0 = tid / VPR;
+        const int cv = tid - row0 * VPR;
+        const char* src = reinterpret_cast<const char*>(stg) + row0 * PITCH_B + cv * 16;
+        const uint32_t voff = (uint32_t)row0 * so_t * ES + cv * 16;
+#pragma unroll
+        for (int j = 0; j < (CP + RPJ - 1) / RPJ; ++j) {
+          if (CP % RPJ == 0 || row0 + j * RPJ < CP) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(src + j * RPJ * PITCH_B);
+            __builtin_amdgcn_raw_buffer_store_b128(val, rs, voff, (int)((uint32_t)(j * RPJ) * so_t * ES), 0);
+          }
+        }
+      };
+      if (f32o) store_rows(std::integral_constant<int, BN * 4 / 16>{}, std::integral_constant<int, 4>{});
+      else store_rows(std::integral_constant<int, BN * 2 / 16>{}, std::integral_constant<int, 2>{});
     }
-    __syncthreads();  // LDS reuse by the next chunk
+    if constexpr (!STG_IN_P) {
+      __syncthreads();  // the staged output has been read
+      if (more) {
+        pfq.store(sQ, tid);
+        pfk.store(sK, tid);
+        pfv.store(sV, tid);
+      }
+      if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
+    }
   }
 
   if (a.s_final) {
