@@ -135,15 +135,26 @@ struct TileStager {
 };
 
 // Causal P tiles in the forward enumeration: t -> (I', J') with J' <= I',
-// t = I'(I'+1)/2 + J'.  Wave-uniform scalar arithmetic.
+// t = I'(I'+1)/2 + J'.  Wave-uniform, branch-free scalar arithmetic.
+template <int CT>
 __device__ __forceinline__ void tile_of(int t, int& Ip, int& Jp) {
   int i = 0;
-  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+#pragma unroll
+  for (int m = 1; m < CT; ++m) i += (t >= m * (m + 1) / 2) ? 1 : 0;
   Ip = i;
   Jp = t - i * (i + 1) / 2;
 }
 
-template <int DK, int DV, int BN, int NW, int C, int NT>
+// P-tile row pitch: the smallest >= CP + 8 (multiple of 8 elements) whose
+// byte pitch mod 256 is 32, 160 or 224 -- conflict-free 16-byte row reads.
+constexpr int pitch_p(int cp) {
+  for (int p = cp + 8;; p += 8) {
+    const int m = (2 * p) % 256;
+    if (m == 32 || m == 160 || m == 224) return p;
+  }
+}
+
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV>
 __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   constexpr int NTHR = NW * 64;
   constexpr int NS = BN / (16 * NW);  // 16-column strips per wave
@@ -156,22 +167,28 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   constexpr int NTP = NT == 3 ? 3 : 2;      // terms of the masked P tile
   constexpr int NTS = NT == 3 ? 3 : 2;      // terms of state fragments
   constexpr int NTK = NT == 3 ? 3 : 2;      // terms of decay-scaled values
-  constexpr int PQ = DKP + 8;               // LDS row pitches (elements)
-  constexpr int PVV = BN + 16;  // column reads of V: conflict-free at this pitch
-  constexpr int PP = CP + 8;
+  // LDS row pitches (elements), chosen from measured bank-conflict rates of
+  // each tile's access mix on gfx950: the query tile is read with 8-byte
+  // row reads, the key tile with 16-byte row reads and column reads, the P
+  // tile with 16-byte row reads, the value tile with column reads.
+  constexpr int PQ = DKP + 8;
+  constexpr int PK = DKP + 16;
+  constexpr int PVV = BN + 16;
+  constexpr int PP = pitch_p(CP);
   constexpr int DKT = DK / 16;  // 16-row tiles of the state
   constexpr int KSD = DKP / 32;  // 32-deep k-steps over DK
   constexpr int CT = CP / 16;    // 16-row tiles of a chunk
   constexpr int KSC = CP / 32;   // 32-deep k-steps over the chunk
   constexpr int NPT = CT * (CT + 1) / 2;  // causal P tiles
   constexpr int MAXPT = (NPT + NW - 1) / NW;
+  constexpr bool TIGHT = DK > 128;  // register-tight shape: pin the schedule
 
   // LDS: query, key and value tiles plus the masked P tile.  When the four do
   // not fit, P is held in registers until every read of the query tile is
   // done and then written over it.
   constexpr int Q_ELEMS = NT * CP * PQ;
   constexpr int P_ELEMS = NTP * CP * PP;
-  constexpr int SEPARATE_BYTES = 2 * (2 * Q_ELEMS + NT * CP * PVV + P_ELEMS) + 4 * (CP + 2);
+  constexpr int SEPARATE_BYTES = 2 * (Q_ELEMS + NT * CP * PK + NT * CP * PVV + P_ELEMS) + 4 * (3 * CP + 2);
   constexpr bool ALIAS_P = SEPARATE_BYTES > 160 * 1024 - 512;
   // output staging (see the store stage): CP rows of BN values at pitch OP2
   // (bf16) or OP4 (fp32)
@@ -182,7 +199,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   constexpr int QP_ELEMS = QP_RAW > STG_ELEMS ? QP_RAW : STG_ELEMS;
   constexpr bool STG_IN_P = !ALIAS_P && STG_ELEMS <= P_ELEMS;
   __shared__ __attribute__((aligned(16))) bf16_t sQP[QP_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16_t sK[NT * CP * PQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[NT * CP * PK];
   __shared__ __attribute__((aligned(16))) bf16_t sV[NT * CP * PVV];
   __shared__ float sPow[CP + 2];
   // per-chunk factor tables for a chunk of L tokens: row factors (how the
@@ -212,17 +229,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   const int l = tid & 63;
   const int g = l >> 4;
   const int li = l & 15;
-  const int rev = a.reverse;
+  constexpr bool rev = REV;  // time direction (a.reverse selected this instantiation)
 
   const float lam = a.lam[h];
   for (int n = tid; n <= CP + 1; n += NTHR) sPow[n] = lam_pow_f32(lam, n);
+  // (reads sPow: every call site is preceded by a barrier after sPow is filled)
   auto fill_factors = [&](int Lc) {
     for (int n = tid; n < CP; n += NTHR) {
       const bool in = n < Lc;
       const int er = rev ? Lc - 1 - n : n + 1;  // row exponent
       const int ec = rev ? n + 1 : Lc - 1 - n;  // column exponent
-      sRowF[n] = in ? lam_pow_f32(lam, er) : 0.0f;
-      sColF[n] = in ? lam_pow_f32(lam, ec) : 0.0f;
+      sRowF[n] = in ? sPow[er] : 0.0f;
+      sColF[n] = in ? sPow[ec] : 0.0f;
     }
   };
   // decay mask of the diagonal P tiles, per lane: forward keeps j <= i with
@@ -293,7 +311,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 
   // The next chunk's tiles are loaded into registers while the current chunk
   // is computed, so HBM latency overlaps the MFMA work.
-  TileStager<NT, CP, DK, DKP, PQ, NTHR> pfq, pfk;
+  TileStager<NT, CP, DK, DKP, PQ, NTHR> pfq;
+  TileStager<NT, CP, DK, DKP, PK, NTHR> pfk;
   TileStager<NT, CP, BN, BN, PVV, NTHR> pfv;
   // With wide query/key rows the three prefetched tiles do not fit in
   // registers next to the state and the P tile; the next query tile is then
@@ -319,6 +338,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     pfq.store(sQ, tid);
     pfk.store(sK, tid);
     pfv.store(sV, tid);
+    __syncthreads();  // sPow complete
     fill_factors(chunk_len(chunk_start(0)));
   }
 
@@ -338,9 +358,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int kt = 0; kt < MAXPT; ++kt) {
       const int t = w + kt * NW;
-      if (t < NPT) {
+      if (NPT % NW == 0 || t < NPT) {
         int Ip, Jp;
-        tile_of(t, Ip, Jp);
+        tile_of<CT>(t, Ip, Jp);
         const int I = rev ? CT - 1 - Ip : Ip;
         const int J = rev ? CT - 1 - Jp : Jp;
         const int i = 16 * I + li;
@@ -350,7 +370,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
           bf16x8 A[NT], Bq[NT];
 #pragma unroll
           for (int p = 0; p < NT; ++p) {
-            A[p] = lds_read_b128(&sK[p * CP * PQ + (16 * J + li) * PQ + 32 * ks + 8 * g]);
+            A[p] = lds_read_b128(&sK[p * CP * PK + (16 * J + li) * PK + 32 * ks + 8 * g]);
             Bq[p] = lds_read_b128(&sQ[p * CP * PQ + i * PQ + 32 * ks + 8 * g]);
           }
           mma_split<NT, NT>(acc, A, Bq);
@@ -369,7 +389,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         if constexpr (ALIAS_P) ptile[kt] = acc;
         else put_p(i, J, acc);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (TIGHT) __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (!ALIAS_P) put_zero_tiles();
 
@@ -399,14 +419,17 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int I = 0; I < CT; ++I) {
         bf16x8 Aq[NT];
+        const int Iph = rev ? CT - 1 - I : I;  // accO[I] holds physical row tile Iph
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
-          const bf16_t* row = &sQ[p * CP * PQ + (16 * I + li) * PQ + 32 * ks];
+          const bf16_t* row = &sQ[p * CP * PQ + (16 * Iph + li) * PQ + 32 * ks];
           Aq[p] = cat4(lds_read_b64(row + 4 * g), lds_read_b64(row + 16 + 4 * g));
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma_split<NTS, NT>(accO[I][s], Sf[s], Aq);
-        if (I % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TIGHT) {
+          if (I % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     {
@@ -419,7 +442,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
           for (int r = 0; r < 4; ++r) accS[D][s][r] *= cfac;
 #pragma unroll
       for (int I = 0; I < CT; ++I) {
-        const int i = 16 * I + li;
+        const int i = 16 * (rev ? CT - 1 - I : I) + li;
         const float f = sRowF[i];
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -433,9 +456,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int kt = 0; kt < MAXPT; ++kt) {
         const int t = w + kt * NW;
-        if (t < NPT) {
+        if (NPT % NW == 0 || t < NPT) {
           int Ip, Jp;
-          tile_of(t, Ip, Jp);
+          tile_of<CT>(t, Ip, Jp);
           const int I = rev ? CT - 1 - Ip : Ip;
           const int J = rev ? CT - 1 - Jp : Jp;
           put_p(16 * I + li, J, ptile[kt]);
@@ -446,8 +469,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     __syncthreads();  // P complete
 
     // ---------------- stage 3: O += P V ; stage 4: S += (colfac K)^T V
-#pragma unroll 1
-    for (int ks = 0; ks < KSC; ++ks) {
+    // Logical k-steps kl and row tiles I keep the causal structure static:
+    // physical k-step ks = rev ? KSC-1-kl : kl, physical row tile
+    // rev ? CT-1-I : I, and row tile I meets k-step kl iff kl <= I / 2.
+    auto kstep = [&](const int kl) {
+      const int ks = rev ? KSC - 1 - kl : kl;
       // V fragments: B[k = 32 ks + 8 g + e][n = strip col + li] via column reads
       bf16x8 Bv[NS][NT];
 #pragma unroll
@@ -462,15 +488,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
       // stage 3 for the row tiles whose causal window touches this k-step
 #pragma unroll
       for (int I = 0; I < CT; ++I) {
-        const bool use = rev ? (ks >= (I >> 1)) : (ks <= (I >> 1));
-        if (!use) continue;
+        if (kl > (I >> 1)) continue;
+        const int Iph = rev ? CT - 1 - I : I;
         bf16x8 Ap[NTP];
 #pragma unroll
         for (int p = 0; p < NTP; ++p)
-          Ap[p] = lds_read_b128(&sP[p * CP * PP + (16 * I + li) * PP + 32 * ks + 8 * g]);
+          Ap[p] = lds_read_b128(&sP[p * CP * PP + (16 * Iph + li) * PP + 32 * ks + 8 * g]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma_split<NT, NTP>(accO[I][s], Bv[s], Ap);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TIGHT) __builtin_amdgcn_sched_barrier(0);
       }
       // stage 4: S += K^T (diag(col factors) V).  The decay rides on this
       // wave's own value strip (split hi/lo); the keys enter exact.
@@ -498,14 +524,25 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         bf16x8 Ak[NT];
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
-          const bf16_t* base = &sK[p * CP * PQ + (32 * ks + 8 * g + (li >> 2)) * PQ + 16 * D + 4 * (li & 3)];
-          Ak[p] = cat4(lds_read_tr(base), lds_read_tr(base + 4 * PQ));
+          const bf16_t* base = &sK[p * CP * PK + (32 * ks + 8 * g + (li >> 2)) * PK + 16 * D + 4 * (li & 3)];
+          Ak[p] = cat4(lds_read_tr(base), lds_read_tr(base + 4 * PK));
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma_split<NT, NTK>(accS[D][s], Ak, Bs[s]);
-        // keep the scheduler from hoisting every row tile's loads at once
-        __builtin_amdgcn_sched_barrier(0);
+        // where registers are tight, keep the scheduler from hoisting every
+        // tile's loads at once
+        if constexpr (TIGHT) __builtin_amdgcn_sched_barrier(0);
       }
+      // one k-step at a time: bounds the loads in flight, hence the registers
+      __builtin_amdgcn_sched_barrier(0);
+        };
+    // where registers are tight, walk the k-steps as a loop; else unroll them
+    if constexpr (TIGHT) {
+#pragma unroll 1
+      for (int kl = 0; kl < KSC; ++kl) kstep(kl);
+    } else {
+#pragma unroll
+      for (int kl = 0; kl < KSC; ++kl) kstep(kl);
     }
 
     // ---------------- next chunk's tiles -> LDS; store O (rows < L)
@@ -518,17 +555,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     // dropped by the hardware range check.
     __syncthreads();  // every wave is done with the P, key and value tiles
     const bool more = ci + 1 < nchunks;
-    if constexpr (LATE_Q) {
-      if (more) prefetch_q(ci + 1);
-    }
     // the factor tables change only when the next chunk's length differs
     const bool refill = more && chunk_len(chunk_start(ci + 1)) != L;
+    if (more) {
+      pfk.store(sK, tid);
+      pfv.store(sV, tid);
+      if constexpr (STG_IN_P && !LATE_Q) pfq.store(sQ, tid);
+      if constexpr (LATE_Q) prefetch_q(ci + 1);  // lands after the output is out
+    }
     if constexpr (STG_IN_P) {
-      if (more) {
-        pfq.store(sQ, tid);
-        pfk.store(sK, tid);
-        pfv.store(sV, tid);
-      }
       if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
     }
     {
@@ -540,7 +575,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         for (int I = 0; I < CT; ++I)
 #pragma unroll
           for (int s = 0; s < NS; ++s)
-            *reinterpret_cast<f32x4*>(&st4[(16 * I + li) * OP4 + (w * NS + s) * 16 + 4 * g]) = accO[I][s];
+            *reinterpret_cast<f32x4*>(&st4[(16 * (rev ? CT - 1 - I : I) + li) * OP4 + (w * NS + s) * 16 + 4 * g]) = accO[I][s];
       } else {
 #pragma unroll
         for (int I = 0; I < CT; ++I)
@@ -549,7 +584,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
             bf16x4 pk;
 #pragma unroll
             for (int r = 0; r < 4; ++r) pk[r] = (__bf16)accO[I][s][r];
-            *reinterpret_cast<bf16x4*>(&stg[(16 * I + li) * OP2 + (w * NS + s) * 16 + 4 * g]) = pk;
+            *reinterpret_cast<bf16x4*>(&stg[(16 * (rev ? CT - 1 - I : I) + li) * OP2 + (w * NS + s) * 16 + 4 * g]) = pk;
           }
       }
       __syncthreads();
@@ -582,12 +617,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     }
     if constexpr (!STG_IN_P) {
       __syncthreads();  // the staged output has been read
-      if (more) {
-        pfq.store(sQ, tid);
-        pfk.store(sK, tid);
-        pfv.store(sV, tid);
-      }
       if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
+    }
+    if constexpr (!STG_IN_P || LATE_Q) {
+      if (more) pfq.store(sQ, tid);
     }
   }
 
@@ -609,7 +642,10 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const int64_t groups = (BH + 7) / 8;
   const int64_t nblocks = groups * 8 * NBLK;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT>), dim3((unsigned)nblocks), dim3(NW * 64), 0, st, a);
+  if (a.reverse)
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false>), dim3((unsigned)nblocks), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -617,7 +653,7 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
 template <int DK, int DV, int C, int NT>
 static hipError_t launch_shape(const ChunkArgs& a, hipStream_t st) {
   if constexpr (DK == 96 && DV == 192) return launch_one<96, 192, 96, 6, C, NT>(a, st);
-  else if constexpr (DK == 192 && DV == 96) return launch_one<192, 96, 96, 6, C, NT>(a, st);
+  else if constexpr (DK == 192 && DV == 96) return launch_one<192, 96, 48, 3, C, NT>(a, st);
   else if constexpr (DK == 16 && DV == 32) return launch_one<16, 32, 32, 2, C, NT>(a, st);
   else if constexpr (DK == 32 && DV == 16) return launch_one<32, 16, 16, 1, C, NT>(a, st);
   else return hipErrorInvalidValue;
