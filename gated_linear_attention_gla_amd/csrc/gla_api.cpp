@@ -16,6 +16,12 @@
 //   dv: query k,  key q,  value dO, state G   (starts at dS_T), reverse time
 //   dk: query v,  key dO, value q,  state G^T (starts at dS_T^T), reverse time
 // and the final state of the dv pass is dS0.
+//
+// Segment split (page section "Challenge 1": the chunks are independent, only
+// the state chain is serial).  When too few (b, h) units exist to fill the
+// GPU, a pass splits the tokens into segments: a state pass computes every
+// segment's end state from a zero start into the workspace, then each
+// segment's full pass starts from lam^len-weighted sums of the earlier ones.
 #include "../../include/gla.h"
 #include "gla_internal.h"
 
@@ -58,6 +64,25 @@ gla_status check_dims(const gla_dims* d) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tokens per segment when a pass is split into nseg segments of whole chunks.
+int64_t seg_len_for(int64_t T, int64_t chunk, int nseg) {
+  const int64_t nchunks = (T + chunk - 1) / chunk;
+  return ((nchunks + nseg - 1) / nseg) * chunk;
+}
+
+// Workspace of one segment-split pass: the end state of every (b, h, segment).
+size_t pass_workspace(const gla_dims* d, int dk, int dv) {
+  const int nseg = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk);
+  if (nseg <= 1) return 0;
+  return (size_t)d->B * d->H * nseg * d->dk * d->dv * sizeof(float);
+}
+
+void set_segments(ChunkArgs& a, const gla_dims* d, int dk, int dv, void* ws) {
+  a.nseg = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk);
+  a.seg_len = a.nseg > 1 ? seg_len_for(d->T, d->chunk, a.nseg) : (d->T > 0 ? d->T : 1);
+  a.seg_state = a.nseg > 1 ? static_cast<float*>(ws) : nullptr;
+}
 
 ChunkArgs make_pass(const gla_dims* d, const gla_tensor* qr, const gla_tensor* kr, const gla_tensor* vr,
                     const float* lambda, const float* s_init, int s_init_trans, float* s_final,
@@ -105,12 +130,15 @@ const char* gla_status_string(gla_status s) {
 
 size_t gla_chunk_fwd_workspace(const gla_dims* dims) {
   if (!dims || check_dims(dims) != GLA_OK) return 0;
-  return 0;
+  return pass_workspace(dims, (int)dims->dk, (int)dims->dv);
 }
 
 size_t gla_chunk_bwd_workspace(const gla_dims* dims) {
   if (!dims || check_dims(dims) != GLA_OK) return 0;
-  return 0;
+  // the three passes run one after another on the stream and share it
+  const size_t a = pass_workspace(dims, (int)dims->dk, (int)dims->dv);
+  const size_t b = pass_workspace(dims, (int)dims->dv, (int)dims->dk);
+  return a > b ? a : b;
 }
 
 gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
@@ -137,10 +165,11 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_te
       same(S_T, o->data) || same(S_T, lambda) || same(o->data, lambda) || same(o->data, S0))
     return GLA_ERR_ALIAS;
   const size_t need_ws = gla_chunk_fwd_workspace(dims);
-  if (ws_bytes < need_ws || (need_ws > 0 && ws == nullptr)) return GLA_ERR_WORKSPACE;
+  if (ws_bytes < need_ws || (need_ws > 0 && (ws == nullptr || !aligned16(ws)))) return GLA_ERR_WORKSPACE;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, o, 0);
+  set_segments(a, dims, (int)dims->dk, (int)dims->dv, ws);
   if (gla::launch_chunk_pass((int)dims->dk, (int)dims->dv, (int)dims->chunk, a, s) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
@@ -177,17 +206,20 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
       if (same(outs[i], outs[j])) return GLA_ERR_ALIAS;
   }
   const size_t need_ws = gla_chunk_bwd_workspace(dims);
-  if (ws_bytes < need_ws || (need_ws > 0 && ws == nullptr)) return GLA_ERR_WORKSPACE;
+  if (ws_bytes < need_ws || (need_ws > 0 && (ws == nullptr || !aligned16(ws)))) return GLA_ERR_WORKSPACE;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // dq: query dO, key v, value k; state S^T from S0^T; forward time
   ChunkArgs a1 = make_pass(dims, dO, v, k, lambda, S0, 1, nullptr, dq, 0);
+  set_segments(a1, dims, DV, DK, ws);
   if (gla::launch_chunk_pass(DV, DK, C, a1, s) != hipSuccess) return GLA_ERR_HIP;
   // dv (and dS0): query k, key q, value dO; state G from dS_T; reverse time
   ChunkArgs a2 = make_pass(dims, k, q, dO, lambda, dS_T, 0, dS0, dv, 1);
+  set_segments(a2, dims, DK, DV, ws);
   if (gla::launch_chunk_pass(DK, DV, C, a2, s) != hipSuccess) return GLA_ERR_HIP;
   // dk: query v, key dO, value q; state G^T from dS_T^T; reverse time
   ChunkArgs a3 = make_pass(dims, v, dO, q, lambda, dS_T, 1, nullptr, dk, 1);
+  set_segments(a3, dims, DV, DK, ws);
   if (gla::launch_chunk_pass(DV, DK, C, a3, s) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }

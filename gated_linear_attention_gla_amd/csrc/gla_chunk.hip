@@ -154,7 +154,9 @@ constexpr int pitch_p(int cp) {
   }
 }
 
-template <int DK, int DV, int BN, int NW, int C, int NT, bool REV>
+// SO (state only): the segment state pass -- only the state update runs, from
+// a zero state, and the segment's end state goes to a.seg_state.
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO>
 __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   constexpr int NTHR = NW * 64;
   constexpr int NS = BN / (16 * NW);  // 16-column strips per wave
@@ -212,15 +214,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 
 
   // XCD-aware block decode: consecutive dispatch slots on one XCD (block ids
-  // congruent mod 8) walk the column blocks of the same (b, h), so the q/k
-  // tiles they share are served from that XCD's L2.
+  // congruent mod 8) walk the segments, then the column blocks, of the same
+  // (b, h), so the tiles and segment states they share are served from that
+  // XCD's L2.
   const int64_t BH = a.B * a.H;
   const int xb = blockIdx.x;
   const int xcd = xb & 7;
+  const int nseg = a.nseg;
   const int slot = xb >> 3;
-  const int64_t bh = (int64_t)(slot / NBLK) * 8 + xcd;
-  const int nblk = slot % NBLK;
+  const int seg = slot % nseg;
+  const int slot2 = slot / nseg;
+  const int64_t bh = (int64_t)(slot2 / NBLK) * 8 + xcd;
+  const int nblk = slot2 % NBLK;
   if (bh >= BH) return;
+  // the state pass produces what later segments (in walk order) consume
+  if (SO && (REV ? seg == 0 : seg == nseg - 1)) return;
   const int64_t b = bh / a.H;
   const int64_t h = bh - b * a.H;
 
@@ -264,7 +272,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   // ---- state slice in accumulators: accS[D][s][r] = S[16 D + 4 g + r][col0 + 16 s]
   f32x4 accS[DKT][NS];
   {
-    const float* si = a.s_init ? a.s_init + bh * (int64_t)DK * DV : nullptr;
+    const float* si = (!SO && a.s_init) ? a.s_init + bh * (int64_t)DK * DV : nullptr;
 #pragma unroll
     for (int D = 0; D < DKT; ++D)
 #pragma unroll
@@ -277,6 +285,25 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
           if (si) x = a.s_init_trans ? si[(int64_t)n * DK + d] : si[(int64_t)d * DV + n];
           accS[D][s][r] = x;
         }
+  }
+  const int64_t T = a.T;
+  // The segments before this one (in walk order) enter through their end
+  // states: S <- lam^len S + E, oldest first.
+  if constexpr (!SO) {
+    const int first = REV ? nseg - 1 : 0;
+    const int step = REV ? -1 : 1;
+    for (int p = first; p != seg; p += step) {
+      const int64_t len = (T - p * a.seg_len) < a.seg_len ? (T - p * a.seg_len) : a.seg_len;
+      const float dec = lam_pow_f32(a.lam[h], (int)len);
+      const float* E = a.seg_state + (bh * nseg + p) * (int64_t)DK * DV;
+#pragma unroll
+      for (int D = 0; D < DKT; ++D)
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            accS[D][s][r] = fmaf(dec, accS[D][s][r], E[(int64_t)(16 * D + 4 * g + r) * DV + col0 + 16 * s]);
+    }
   }
 
   // writes 4 consecutive masked-P values of row i (cols 16 J + 4 g ..) as NTP planes
@@ -303,11 +330,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     }
   };
 
-  const int64_t T = a.T;
-  const int64_t nchunks = (T + C - 1) / C;
+  // this segment's tokens [tb, te) and their chunks
+  const int64_t tb = (int64_t)seg * a.seg_len;
+  const int64_t te = (T - tb) < a.seg_len ? T : tb + a.seg_len;
+  const int64_t nchunks = (te - tb + C - 1) / C;
   // chunk ci of the walk (reverse time walks the chunks backwards)
-  auto chunk_start = [&](int64_t ci) { return (rev ? (nchunks - 1 - ci) : ci) * C; };
-  auto chunk_len = [&](int64_t t0) { return (int)((T - t0) < C ? (T - t0) : C); };
+  auto chunk_start = [&](int64_t ci) { return tb + (rev ? (nchunks - 1 - ci) : ci) * C; };
+  auto chunk_len = [&](int64_t t0) { return (int)((te - t0) < C ? (te - t0) : C); };
 
   // The next chunk's tiles are loaded into registers while the current chunk
   // is computed, so HBM latency overlaps the MFMA work.
@@ -333,9 +362,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   // done; the output of chunk ci is stored last, so its write latency
   // overlaps the compute of chunk ci+1.
   if (nchunks > 0) {
-    prefetch_q(0);
+    if constexpr (!SO) prefetch_q(0);
     prefetch_kv(0);
-    pfq.store(sQ, tid);
+    if constexpr (!SO) pfq.store(sQ, tid);
     pfk.store(sK, tid);
     pfv.store(sV, tid);
     __syncthreads();  // sPow complete
@@ -349,12 +378,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     // ---------------- stage 0: this chunk's tiles are in LDS; start the next loads
     __syncthreads();
     if (ci + 1 < nchunks) {
-      if constexpr (!LATE_Q) prefetch_q(ci + 1);
+      if constexpr (!LATE_Q && !SO) prefetch_q(ci + 1);
       prefetch_kv(ci + 1);
     }
 
     // ---------------- stage 1: masked P tiles (causal half), P[i][j] row-major
     f32x4 ptile[ALIAS_P ? MAXPT : 1];
+    if constexpr (!SO) {
 #pragma unroll
     for (int kt = 0; kt < MAXPT; ++kt) {
       const int t = w + kt * NW;
@@ -393,12 +423,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     }
     if constexpr (!ALIAS_P) put_zero_tiles();
 
+    }
+
     // ---------------- stage 2: O^T = S^T Q^T, rows scaled by the row factors
     f32x4 accO[CT][NS];
 #pragma unroll
     for (int I = 0; I < CT; ++I)
 #pragma unroll
       for (int s = 0; s < NS; ++s) accO[I][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!SO) {
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
       // State as the B operand of Q S: k-slot e of lane group g holds state
@@ -432,6 +465,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         }
       }
     }
+    }
     {
       const float cfac = sPow[L];
 #pragma unroll
@@ -440,18 +474,20 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         for (int s = 0; s < NS; ++s)
 #pragma unroll
           for (int r = 0; r < 4; ++r) accS[D][s][r] *= cfac;
+      if constexpr (!SO) {
 #pragma unroll
-      for (int I = 0; I < CT; ++I) {
-        const int i = 16 * (rev ? CT - 1 - I : I) + li;
-        const float f = sRowF[i];
+        for (int I = 0; I < CT; ++I) {
+          const int i = 16 * (rev ? CT - 1 - I : I) + li;
+          const float f = sRowF[i];
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+          for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) accO[I][s][r] *= f;
+            for (int r = 0; r < 4; ++r) accO[I][s][r] *= f;
+        }
       }
     }
 
-    if constexpr (ALIAS_P) {
+    if constexpr (ALIAS_P && !SO) {
       __syncthreads();  // every read of the query tile is done
 #pragma unroll
       for (int kt = 0; kt < MAXPT; ++kt) {
@@ -466,7 +502,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
       }
       put_zero_tiles();
     }
-    __syncthreads();  // P complete
+    if constexpr (!SO) __syncthreads();  // P complete
 
     // ---------------- stage 3: O += P V ; stage 4: S += (colfac K)^T V
     // Logical k-steps kl and row tiles I keep the causal structure static:
@@ -488,7 +524,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
       // stage 3 for the row tiles whose causal window touches this k-step
 #pragma unroll
       for (int I = 0; I < CT; ++I) {
-        if (kl > (I >> 1)) continue;
+        if (SO || kl > (I >> 1)) continue;
         const int Iph = rev ? CT - 1 - I : I;
         bf16x8 Ap[NTP];
 #pragma unroll
@@ -560,13 +596,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     if (more) {
       pfk.store(sK, tid);
       pfv.store(sV, tid);
-      if constexpr (STG_IN_P && !LATE_Q) pfq.store(sQ, tid);
-      if constexpr (LATE_Q) prefetch_q(ci + 1);  // lands after the output is out
+      if constexpr (STG_IN_P && !LATE_Q && !SO) pfq.store(sQ, tid);
+      if constexpr (LATE_Q && !SO) prefetch_q(ci + 1);  // lands after the output is out
     }
     if constexpr (STG_IN_P) {
       if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
     }
-    {
+    if constexpr (!SO) {
       const int f32o = a.o_f32;
       bf16_t* stg = STG_IN_P ? sP : sQP;
       if (f32o) {
@@ -619,13 +655,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
       __syncthreads();  // the staged output has been read
       if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
     }
-    if constexpr (!STG_IN_P || LATE_Q) {
+    if constexpr ((!STG_IN_P || LATE_Q) && !SO) {
       if (more) pfq.store(sQ, tid);
     }
   }
 
-  if (a.s_final) {
-    float* sf = a.s_final + bh * (int64_t)DK * DV;
+  // the state pass hands its segment's end state to the later segments; the
+  // last segment in walk order returns the final state
+  float* dst = nullptr;
+  if constexpr (SO) dst = a.seg_state + (bh * nseg + seg) * (int64_t)DK * DV;
+  else if (a.s_final && seg == (REV ? 0 : nseg - 1)) dst = a.s_final + bh * (int64_t)DK * DV;
+  if (dst) {
+    float* sf = dst;
 #pragma unroll
     for (int D = 0; D < DKT; ++D)
 #pragma unroll
@@ -640,13 +681,39 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   constexpr int NBLK = DV / BN;
   const int64_t BH = a.B * a.H;
   const int64_t groups = (BH + 7) / 8;
-  const int64_t nblocks = groups * 8 * NBLK;
+  const int64_t nblocks = groups * 8 * NBLK * a.nseg;
   if (nblocks <= 0) return hipSuccess;
-  if (a.reverse)
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false>), dim3((unsigned)nblocks), dim3(NW * 64), 0, st, a);
+  const dim3 grid((unsigned)nblocks), block(NW * 64);
+  if (a.nseg > 1) {
+    if (a.reverse) hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false, true>), grid, block, 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.reverse) hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, true, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false, false>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+// column-block width per shape (must match launch_shape)
+static int block_cols(int dk, int dv) {
+  if (dk == 96 && dv == 192) return 96;
+  if (dk == 192 && dv == 96) return 48;
+  return dv;  // the small shapes run all columns in one workgroup
+}
+
+int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk) {
+  constexpr int64_t kTargetUnits = 256;  // one workgroup per compute unit of an MI355X
+  const int64_t units = B * H * (dv / block_cols(dk, dv));
+  const int64_t nchunks = (T + chunk - 1) / chunk;
+  if (units >= kTargetUnits || nchunks < 4) return 1;
+  int64_t nseg = (kTargetUnits + units - 1) / units;
+  if (nseg > nchunks / 2) nseg = nchunks / 2;  // at least two chunks per segment
+  if (nseg > 64) nseg = 64;
+  if (nseg < 2) return 1;
+  // equal segments of whole chunks; drop any that would be empty
+  const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
+  return (int)((nchunks + seg_chunks - 1) / seg_chunks);
 }
 
 // Tile shapes per (DK, DV): BN columns per workgroup, NW waves.

@@ -29,6 +29,14 @@ struct ChunkArgs {
   int reverse;            // 0: tokens 0..T-1, 1: tokens T-1..0
   int o_f32;              // output storage: 1 fp32, 0 bf16
   int in_f32;             // input storage:  1 fp32, 0 bf16 (must match the instantiation)
+  // Segment-parallel form: tokens split into nseg segments of seg_len tokens
+  // (a multiple of the chunk; the last may be shorter).  seg_state holds,
+  // per (b, h) and segment, the segment's end state from a zero start
+  // ([B][H][nseg] x (DK x DV), fp32); the state pass writes it and the full
+  // pass folds the earlier segments' states into its entry state.
+  int nseg;
+  int64_t seg_len;
+  float* seg_state;
 };
 
 struct DecodeArgs {
@@ -48,7 +56,12 @@ struct DecodeArgs {
 
 // Launchers return hipSuccess or the launch error.  They perform no
 // validation: the C-ABI layer checks every argument first.
+// One chunked pass; with a.nseg > 1 this is the segment state pass followed
+// by the full pass.
 hipError_t launch_chunk_pass(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st);
+// Segments used for these dims (1 = no segment split) and the workspace bytes
+// they need: enough (b, h, column block, segment) units to fill the GPU.
+int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk);
 bool chunk_pass_supported(int dk, int dv, int chunk, int in_f32);
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
 bool decode_supported(int dk, int dv);

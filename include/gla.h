@@ -97,7 +97,15 @@ int gla_abi_version(void);
 const char* gla_status_string(gla_status s);
 
 /* Bytes of device workspace gla_chunk_fwd needs for these dims (0 if none).
- * Returns 0 for dims that gla_chunk_fwd would reject. */
+ * Returns 0 for dims that gla_chunk_fwd would reject.
+ * When B * H is too small to occupy the GPU, a pass splits every sequence
+ * into nseg segments of whole chunks (2 <= nseg <= 64, at least two chunks
+ * each; page section "Challenge 1": the chunks are independent apart from the
+ * state they hand on).  A first launch writes each segment's end state from a
+ * zero start; the second starts segment j from the decayed sum of the end
+ * states before it.  The workspace holds those states: B*H*nseg*dk*dv fp32
+ * values; ws must be 16-byte aligned (GLA_ERR_WORKSPACE otherwise).  Its
+ * contents are scratch and are not needed after the call completes. */
 size_t gla_chunk_fwd_workspace(const gla_dims* dims);
 
 /* Chunked forward (page sections "GLA mixer" and "Challenge 1").
@@ -113,7 +121,8 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_te
                          const gla_tensor* v, const float* lambda, const float* S0,
                          gla_tensor* o, float* S_T, void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of device workspace gla_chunk_bwd needs (0 if none). */
+/* Bytes of device workspace gla_chunk_bwd needs (0 if none): the largest
+ * segment-state buffer of its three passes (see gla_chunk_fwd_workspace). */
 size_t gla_chunk_bwd_workspace(const gla_dims* dims);
 
 /* Chunked backward (page section "Challenge 3") of the scalar

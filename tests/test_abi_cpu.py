@@ -132,6 +132,43 @@ def test_workspace_queries(lib):
     assert lib.gla_chunk_fwd_workspace(ctypes.byref(dims(B=0))) == 0
 
 
+def test_workspace_segment_rule(lib):
+    """The workspace holds one fp32 dk x dv end state per (b, h, segment).  No
+    split when the (b, h, column block) units already fill the GPU or the
+    sequence has fewer than 4 chunks; otherwise 2 to 64 segments of at least
+    2 whole chunks, and the segment length never leaves an empty segment."""
+    per = lambda B, H: B * H * 96 * 192 * 4
+    q = lambda **kw: lib.gla_chunk_fwd_workspace(ctypes.byref(dims(dk=96, dv=192, **kw)))
+    assert q(B=8, H=16, Tn=2048, chunk=128) == 0           # 256 units: no split
+    assert q(B=1, H=16, Tn=3 * 128, chunk=128) == 0        # 3 chunks: no split
+    assert q(B=1, H=16, Tn=0, chunk=128) == 0
+    assert q(B=1, H=16, Tn=2048, chunk=128) == per(1, 16) * 8
+    assert q(B=1, H=16, Tn=65536, chunk=128) == per(1, 16) * 8
+    assert q(B=1, H=2, Tn=16384, chunk=128) == per(1, 2) * 64
+    for T in range(1, 3000, 37):
+        for chunk in (16, 64, 128):
+            n = q(B=1, H=2, Tn=T, chunk=chunk) // per(1, 2)
+            nchunks = -(-T // chunk)
+            if n == 0:
+                assert nchunks < 4
+                continue
+            assert 2 <= n <= min(64, nchunks // 2)
+            seg = -(-nchunks // n)                   # whole chunks per segment
+            assert (n - 1) * seg < nchunks <= n * seg   # the last segment is non-empty
+    d = dims(B=1, H=2, Tn=1000, dk=96, dv=192, chunk=64)
+    assert lib.gla_chunk_bwd_workspace(ctypes.byref(d)) >= lib.gla_chunk_fwd_workspace(ctypes.byref(d))
+
+
+def test_fwd_workspace_checks(lib):
+    d = dims(Tn=1000, chunk=64)
+    need = lib.gla_chunk_fwd_workspace(ctypes.byref(d))
+    assert need > 0
+    q, k, v, o = views(Tn=1000)
+    assert fwd(lib, d, q, k, v, o) == WS                                  # missing
+    assert fwd(lib, d, q, k, v, o, ws=0x800000, nws=need - 4) == WS      # too small
+    assert fwd(lib, d, q, k, v, o, ws=0x800008, nws=need) == WS          # misaligned
+
+
 def bwd(lib, d, q, k, v, dO, dq, dk, dv, lam=0x9000, S0=None, dST=None, dS0=None):
     ref = lambda x: None if x is None else ctypes.byref(x)
     return lib.gla_chunk_bwd(ref(d), ref(q), ref(k), ref(v), lam, S0, ref(dO), dST,

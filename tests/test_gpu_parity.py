@@ -5,6 +5,8 @@ Gate (per output tensor, max|err| / max|ref| in fp64): 2e-3 for bf16 inputs,
 must equal the round-to-nearest-even of the fp32-stored run (within one bf16
 ulp, for the accumulation order may differ between the two launches).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -185,6 +187,63 @@ def test_bwd_training_full_sampled(gla):
         errs = [oracle.rel_err(a[sl], rr) for a, rr in zip(g, r)]
         flush(f"  b={b} err dq/dk/dv/dS0 = " + " ".join(f"{e:.3e}" for e in errs))
         assert max(errs) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------ segment split
+# With few (b, h) units the library splits each sequence into segments of
+# whole chunks (a state pass, then a full pass whose entry state folds the
+# earlier segments' end states).  These cases pick T so that the last segment
+# is ragged, segments are dropped by the rounding of the segment length, and
+# the reverse-time passes of the backward carry dS0 across segments.
+def segments_of(gla, B, H, T, dk, dv, chunk, bwd=False):
+    """Segments per (b, h) implied by the workspace query (end states, fp32)."""
+    lib, d = gla.load_library(), ctypes.byref(gla.GlaDims(B, H, T, dk, dv, chunk))
+    nws = lib.gla_chunk_bwd_workspace(d) if bwd else lib.gla_chunk_fwd_workspace(d)
+    return nws // (B * H * dk * dv * 4)
+
+
+@pytest.mark.parametrize("T,chunk", [(1000, 32), (1000, 128), (9 * 64 - 5, 64), (4 * 16, 16)])
+def test_fwd_segments_bf16(gla, T, chunk):
+    flush(f"test_fwd_segments_bf16 T={T} chunk={chunk}")
+    x = inputs.random_chunk_inputs(400 + T, 1, 2, T, 96, 192, dtype="bf16", scale=0.3)
+    assert segments_of(gla, 1, 2, T, 96, 192, chunk) >= 2
+    check_fwd(gla, x, "bf16", chunk)
+
+
+@pytest.mark.parametrize("lam", [0.0, 1.0, 0.999])
+def test_fwd_segments_lambda_edges_fp32(gla, lam):
+    flush(f"test_fwd_segments_lambda_edges_fp32 lam={lam}")
+    x = inputs.random_chunk_inputs(410, 1, 1, 1500, 16, 32, dtype="f32", lam=np.full(1, lam))
+    assert segments_of(gla, 1, 1, 1500, 16, 32, 16) == 47
+    check_fwd(gla, x, "f32", 16)
+
+
+def test_fwd_segments_long_decay(gla):
+    """T=16,384 at B=1, slowest heads of the long-context decay profile: 64
+    segments whose entry states are sums over up to 63 earlier ones."""
+    flush("test_fwd_segments_long_decay")
+    x = inputs.make_chunk_inputs("long", T=16384)
+    for key in ("q", "k", "v"):
+        x[key] = x[key][:, -2:]
+    x["lam"] = x["lam"][-2:]
+    x["S0"] = inputs.normal(411, inputs.TID["S"], (1, 2, 96, 192), 0.01, "f32")
+    assert segments_of(gla, 1, 2, 16384, 96, 192, 128) == 64
+    check_fwd(gla, x, "bf16", 128)
+
+
+@pytest.mark.parametrize("T,chunk", [(777, 64), (1000, 128), (300, 32)])
+def test_bwd_segments_bf16(gla, T, chunk):
+    flush(f"test_bwd_segments_bf16 T={T} chunk={chunk}")
+    x = inputs.random_chunk_inputs(420 + T, 1, 2, T, 96, 192, dtype="bf16", dS_T=True, scale=0.5)
+    assert segments_of(gla, 1, 2, T, 96, 192, chunk, bwd=True) >= 2
+    check_bwd(gla, x, "bf16", chunk)
+
+
+def test_bwd_segments_fp32(gla):
+    flush("test_bwd_segments_fp32")
+    x = inputs.random_chunk_inputs(430, 1, 1, 1001, 16, 32, dtype="f32", dS_T=True)
+    assert segments_of(gla, 1, 1, 1001, 16, 32, 16, bwd=True) == 21
+    check_bwd(gla, x, "f32", 16)
 
 
 # ------------------------------------------------------------------ decode
