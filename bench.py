@@ -9,6 +9,7 @@ of fp32 96x192 states, 64 steps) and reports it under "decode", and times
 the fp64 CPU oracle on a bounded sample under "cpu_baseline".
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-decode] [--no-cpu]
+                    [--decode-steps N] [--calibrate-copy]
 """
 import argparse
 import json
@@ -181,6 +182,49 @@ def bench_decode(gla, inputs, steps_override=None):
     )
 
 
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of nbytes (read nbytes, write nbytes):
+    the reference dispatch that scales the HBM byte counters of a
+    rocprofv3 --pmc run (FETCH_SIZE, WRITE_SIZE) to bytes."""
+    import torch
+
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return dict(bytes=nbytes, reps=reps)
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources; traffic figures are only valid for the
+    sources they were counted on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(REPO, "gated_linear_attention_gla_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+TRAFFIC_FILE = os.path.join(REPO, "profiles", "chunk_kernel_bwd_training_traffic.json")
+
+
+def counted_traffic():
+    """HBM bytes per backward call from the committed counter summary, or
+    None when it is missing or was counted on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return t.get("bwd_call_bytes")
+
+
 def cpu_baseline(inputs, min_seconds=5.0):
     """The fp64 oracle (token recurrence forward + two-sweep backward) on the
     training workload itself (B=8, 16 heads, 2,048 tokens; same recipe and
@@ -212,6 +256,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -238,6 +284,9 @@ def main():
         log("bench: decode")
         dec = bench_decode(gla, inputs, args.decode_steps)
         log(f"  {dec['ms_total']:.1f} ms  {dec['gbs']:.0f} GB/s")
+    if args.calibrate_copy:
+        log("bench: 1 GiB copy (counter calibration)")
+        copy_calibration()
     cpu = None
     if not args.no_cpu:
         log("bench: cpu oracle baseline")
@@ -281,7 +330,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": dom["achieved"] / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": counted_traffic() if dom["kernel"].startswith("gla_chunk_bwd") else None,
             "bytes_per_launch": dom["bytes_per_launch"],
             "ms_per_launch": dom["ms_per_launch"],
         },
