@@ -1,12 +1,14 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
 A step is one chunked forward + backward (gla_chunk_fwd + gla_chunk_bwd) on
-the training-shape workload: B=8, H=16, T=2048, dk=96, dv=192, chunk=128,
-bf16 q/k/v/dO, fp32 states, seeded synthetic inputs resident in HBM.  The
-JSON line's value is whole-step tokens/s (B*T per step).  The same run also
-measures the batched decode workload (1,280 sequences x 24 layers x 16 heads
-of fp32 96x192 states, 64 steps) and reports it under "decode", and times
-the fp64 CPU oracle on a bounded sample under "cpu_baseline".
+the training-shape workload: B=8, H=16, T=2048, dk=96, dv=192, bf16
+q/k/v/dO, fp32 states, seeded synthetic inputs resident in HBM, 64-token
+chunks (the same step at the pages' 128-token chunk is reported under
+"extra").  The JSON line's value is whole-step tokens/s (B*T per step).  The
+same run also measures the batched decode workload (1,280 sequences x 24
+layers x 16 heads of fp32 96x192 states, 64 steps) and reports it under
+"decode", and times the fp64 CPU oracle on a bounded sample under
+"cpu_baseline".
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-decode] [--no-cpu]
                     [--decode-steps N] [--calibrate-copy]
@@ -25,14 +27,26 @@ METRIC = "GLA fwd+bwd tokens/s (H=16,dk=96,dv=192) + decode tok/s, % roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 
-# algorithmic work per token-head (one token of one head), chunk C = 128
-C = 128
+# Chunk length of every timed call.  The output does not depend on it beyond
+# rounding (the tests check 16, 32, 64 and 128 against the oracle); the pages'
+# 128-token chunk matched Trainium's 128 SBUF partitions, while on gfx950 the
+# 64-token chunk keeps the backward's transposed passes in registers and runs
+# faster.  The 128-token chunk is timed as well and reported under "extra".
+C = 64
+C_PAGE = 128
 DK, DV = 96, 192
 FWD_BYTES = 2 * (DK + DK + DV + DV)  # q, k, v in; o out (bf16)
 BWD_BYTES = 2 * (DK + DK + DV + DV) + 2 * (DK + DK + DV)  # q, k, v, dO in; dq, dk, dv out
 STATE_BYTES = DK * DV * 4
-FWD_FLOPS = 2 * C * (DK + DV) + 4 * DK * DV
-BWD_FLOPS = 2 * C * (3 * DK + 2 * DV) + 8 * DK * DV
+# algorithmic work per token-head (one token of one head) at chunk c
+def FWD_FLOPS(c):
+    return 2 * c * (DK + DV) + 4 * DK * DV
+
+
+def BWD_FLOPS(c):
+    return 2 * c * (3 * DK + 2 * DV) + 8 * DK * DV
+
+
 DEC_BYTES = 2 * STATE_BYTES + 2 * (DK + DK + DV) + 2 * DV + 4  # state r+w, q k v, o, lambda
 
 
@@ -55,7 +69,7 @@ def event_time_ms(fn, n, stream):
     return s.elapsed_time(e) / n
 
 
-def bench_train(gla, inputs, steps, warmup):
+def bench_train(gla, inputs, steps, warmup, chunk=C):
     import numpy as np
     import torch
 
@@ -72,10 +86,10 @@ def bench_train(gla, inputs, steps, warmup):
     stream = torch.cuda.current_stream()
 
     def fwd():
-        gla.chunk_fwd(q, k, v, lam, S0, chunk=C, o=o, S_T=S_T)
+        gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, o=o, S_T=S_T)
 
     def bwd():
-        gla.chunk_bwd(q, k, v, lam, dO, S0, None, chunk=C, dq=dq, dk=dk, dv=dv, dS0=dS0)
+        gla.chunk_bwd(q, k, v, lam, dO, S0, None, chunk=chunk, dq=dq, dk=dk, dv=dv, dS0=dS0)
 
     def step():
         fwd()
@@ -101,13 +115,43 @@ def bench_train(gla, inputs, steps, warmup):
         tokens_per_s=B * T / (ms_step / 1e3),
         fwd_bytes=units * FWD_BYTES + 2 * B * H * STATE_BYTES,
         bwd_bytes=units * BWD_BYTES + 2 * B * H * STATE_BYTES,
-        fwd_flops=units * FWD_FLOPS, bwd_flops=units * BWD_FLOPS,
+        fwd_flops=units * FWD_FLOPS(chunk), bwd_flops=units * BWD_FLOPS(chunk), chunk=chunk,
         lam=[float(t) for t in x["lam"]],
     )
     return res
 
 
-def bench_fwd_only(gla, inputs, name, reps):
+def bench_fwd_bwd_events(gla, inputs, name, reps, chunk=C):
+    """Event-timed forward and backward calls of a chunked training-shape
+    workload (the page's decay-schedule variant of the step, and the step at
+    the pages' 128-token chunk)."""
+    import numpy as np
+    import torch
+
+    x = inputs.make_chunk_inputs(name, with_grad=True)
+    cfg = x["cfg"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    q, k, v, dO = (d(x[n]).to(torch.bfloat16) for n in ("q", "k", "v", "dO"))
+    lam, S0 = d(x["lam"]), d(x["S0"])
+    o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
+    dq, dk, dv, dS0 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(S0)
+    fwd = lambda: gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, o=o, S_T=S_T)
+    bwd = lambda: gla.chunk_bwd(q, k, v, lam, dO, S0, None, chunk=chunk, dq=dq, dk=dk, dv=dv, dS0=dS0)
+    for _ in range(3):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms_fwd = event_time_ms(fwd, reps, stream)
+    ms_bwd = event_time_ms(bwd, reps, stream)
+    return dict(workload=name, B=B, H=H, T=T, chunk=chunk, ms_fwd=ms_fwd, ms_bwd=ms_bwd,
+                tokens_per_s=B * T / ((ms_fwd + ms_bwd) / 1e3),
+                lam=[float(t) for t in x["lam"]])
+
+
+def bench_fwd_only(gla, inputs, name, reps, chunk=C):
     import numpy as np
     import torch
 
@@ -120,14 +164,14 @@ def bench_fwd_only(gla, inputs, name, reps):
     S0 = d(x["S0"]) if x["S0"] is not None else None
     o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
     S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
-    fn = lambda: gla.chunk_fwd(q, k, v, lam, S0, chunk=C, o=o, S_T=S_T)
+    fn = lambda: gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, o=o, S_T=S_T)
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
     ms = event_time_ms(fn, reps, torch.cuda.current_stream())
     units = B * H * T
     nbytes = units * FWD_BYTES + (2 if S0 is not None else 1) * B * H * STATE_BYTES
-    return dict(workload=name, B=B, H=H, T=T, ms=ms, tokens_per_s=B * T / (ms / 1e3),
+    return dict(workload=name, B=B, H=H, T=T, chunk=chunk, ms=ms, tokens_per_s=B * T / (ms / 1e3),
                 gbs=nbytes / (ms / 1e3) / 1e9, hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
 
 
@@ -275,10 +319,16 @@ def main():
     tr = bench_train(gla, inputs, args.steps, args.warmup)
     log(f"  step {tr['ms_step']:.3f} ms  fwd {tr['ms_fwd']:.3f} ms  bwd {tr['ms_bwd']:.3f} ms")
     extra = {}
-    for name, reps in (("laplace", 50), ("long", 5)):
+    for name, reps in (("laplace", 50), ("long", 20)):
         log(f"bench: {name} fwd")
         extra[name + "_fwd"] = bench_fwd_only(gla, inputs, name, reps)
         log(f"  {extra[name + '_fwd']['ms']:.3f} ms")
+    log(f"bench: training shape fwd+bwd at the pages' {C_PAGE}-token chunk")
+    extra["training_chunk128"] = bench_fwd_bwd_events(gla, inputs, "training", 20, chunk=C_PAGE)
+    log(f"  fwd {extra['training_chunk128']['ms_fwd']:.3f} ms  bwd {extra['training_chunk128']['ms_bwd']:.3f} ms")
+    log("bench: page decay schedule, training shape fwd+bwd")
+    extra["schedule_fwd_bwd"] = bench_fwd_bwd_events(gla, inputs, "schedule", 20)
+    log(f"  fwd {extra['schedule_fwd_bwd']['ms_fwd']:.3f} ms  bwd {extra['schedule_fwd_bwd']['ms_bwd']:.3f} ms")
     dec = None
     if not args.no_decode:
         log("bench: decode")
@@ -318,8 +368,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "training-shape chunked GLA fwd+bwd, B=8 H=16 T=2048 dk=96 dv=192 "
-                        "chunk=128, bf16 q/k/v/dO, fp32 state",
+            "workload": f"training-shape chunked GLA fwd+bwd, B=8 H=16 T=2048 dk=96 dv=192 "
+                        f"chunk={C}, bf16 q/k/v/dO, fp32 state",
+            "chunk_note": f"chunk {C}: results are chunk-invariant up to rounding (tested at 16/32/64/128); "
+                          f"the pages' {C_PAGE}-token chunk is timed under extra.training_chunk128",
             "global_batch": tr["B"], "seq_len": tr["T"], "heads": tr["H"], "dk": DK, "dv": DV,
             "chunk": C, "parallelism": "single GPU",
         },

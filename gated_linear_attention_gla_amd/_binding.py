@@ -152,7 +152,7 @@ def _state_ok(S, B, H, dk, dv, name):
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {(B, H, dk, dv)}")
 
 
-def chunk_fwd(q, k, v, lam, S0=None, chunk=128, out_dtype=None, o=None, S_T=None,
+def chunk_fwd(q, k, v, lam, S0=None, chunk=64, out_dtype=None, o=None, S_T=None,
               return_state=True):
     """o, S_T = chunk_fwd(q, k, v, lam, S0): chunked Simple GLA forward.
 
@@ -179,7 +179,7 @@ def chunk_fwd(q, k, v, lam, S0=None, chunk=128, out_dtype=None, o=None, S_T=None
     return o, S_T
 
 
-def chunk_bwd(q, k, v, lam, dO, S0=None, dS_T=None, chunk=128, grad_dtype=None,
+def chunk_bwd(q, k, v, lam, dO, S0=None, dS_T=None, chunk=64, grad_dtype=None,
               need_dS0=True, dq=None, dk=None, dv=None, dS0=None):
     """dq, dk, dv, dS0 = chunk_bwd(...): gradients of sum <dO, o> + <dS_T, S_T>."""
     lib = load_library()

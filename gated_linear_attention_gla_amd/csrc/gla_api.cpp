@@ -135,9 +135,10 @@ size_t gla_chunk_fwd_workspace(const gla_dims* dims) {
 
 size_t gla_chunk_bwd_workspace(const gla_dims* dims) {
   if (!dims || check_dims(dims) != GLA_OK) return 0;
-  // the three passes run one after another on the stream and share it
+  // the dq and dk passes run together (one buffer each), then the dv pass
+  // reuses the space
   const size_t a = pass_workspace(dims, (int)dims->dk, (int)dims->dv);
-  const size_t b = pass_workspace(dims, (int)dims->dv, (int)dims->dk);
+  const size_t b = 2 * pass_workspace(dims, (int)dims->dv, (int)dims->dk);
   return a > b ? a : b;
 }
 
@@ -212,15 +213,16 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
   // dq: query dO, key v, value k; state S^T from S0^T; forward time
   ChunkArgs a1 = make_pass(dims, dO, v, k, lambda, S0, 1, nullptr, dq, 0);
   set_segments(a1, dims, DV, DK, ws);
-  if (gla::launch_chunk_pass(DV, DK, C, a1, s) != hipSuccess) return GLA_ERR_HIP;
+  // dk: query v, key dO, value q; state G^T from dS_T^T; reverse time
+  ChunkArgs a3 = make_pass(dims, v, dO, q, lambda, dS_T, 1, nullptr, dk, 1);
+  set_segments(a3, dims, DV, DK, ws);
+  if (a3.seg_state) a3.seg_state += pass_workspace(dims, DV, DK) / sizeof(float);
+  // the two share the transposed shape and run in one launch
+  if (gla::launch_chunk_pair(DV, DK, C, a1, a3, s) != hipSuccess) return GLA_ERR_HIP;
   // dv (and dS0): query k, key q, value dO; state G from dS_T; reverse time
   ChunkArgs a2 = make_pass(dims, k, q, dO, lambda, dS_T, 0, dS0, dv, 1);
   set_segments(a2, dims, DK, DV, ws);
   if (gla::launch_chunk_pass(DK, DV, C, a2, s) != hipSuccess) return GLA_ERR_HIP;
-  // dk: query v, key dO, value q; state G^T from dS_T^T; reverse time
-  ChunkArgs a3 = make_pass(dims, v, dO, q, lambda, dS_T, 1, nullptr, dk, 1);
-  set_segments(a3, dims, DV, DK, ws);
-  if (gla::launch_chunk_pass(DV, DK, C, a3, s) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
 

@@ -154,29 +154,81 @@ constexpr int pitch_p(int cp) {
   }
 }
 
-// SO (state only): the segment state pass -- only the state update runs, from
-// a zero state, and the segment's end state goes to a.seg_state.
+// State row held in accumulator slot r of row tile D by lane group g.  With DK
+// a multiple of 32 the two tiles of each 32-row block interleave in runs of 4
+// (tile 2m + h, group g: rows 32 m + 8 g + 4 h + r), so the 8 k-slots a lane
+// group feeds to the readout are 8 consecutive state rows and the query is
+// read with one 16-byte LDS read per fragment; otherwise tile D holds rows
+// 16 D + 4 g + r.
+template <int DK>
+__device__ __forceinline__ int state_row(int D, int g, int r) {
+  if constexpr (DK % 32 == 0) return 32 * (D >> 1) + 8 * g + 4 * (D & 1) + r;
+  else return 16 * D + 4 * g + r;
+}
+
+// LDS layout of one chunk pass: query, key and value tiles plus the masked P
+// tile (bf16 planes), the lam^n table and the per-chunk factor tables.
+template <int DK, int BN, int C, int NT>
+struct ChunkLds {
+  static constexpr int CP = (C + 31) / 32 * 32;    // chunk rows padded to the 32-deep k-step
+  static constexpr int DKP = (DK + 31) / 32 * 32;  // DK padded likewise
+  static constexpr int NTP = NT == 3 ? 3 : 2;      // terms of the masked P tile
+  // LDS row pitches (elements), chosen from measured bank-conflict rates of
+  // each tile's access mix on gfx950: the query tile is read with 16-byte row
+  // reads, the key tile with 16-byte row reads and column reads, the P tile
+  // with 16-byte row reads, the value tile with column reads.
+  static constexpr int PQ = DKP + 8;
+  static constexpr int PK = DKP + 16;
+  static constexpr int PVV = BN + 16;
+  static constexpr int PP = pitch_p(CP);
+  static constexpr int Q_ELEMS = NT * CP * PQ;
+  static constexpr int K_ELEMS = NT * CP * PK;
+  static constexpr int V_ELEMS = NT * CP * PVV;
+  static constexpr int P_ELEMS = NTP * CP * PP;
+  // When the four tiles do not fit, P is held in registers until every read
+  // of the query tile is done and then written over it.
+  static constexpr int SEPARATE_BYTES = 2 * (Q_ELEMS + K_ELEMS + V_ELEMS + P_ELEMS) + 4 * (3 * CP + 2);
+  static constexpr bool ALIAS_P = SEPARATE_BYTES > 160 * 1024 - 512;
+  // output staging (see the store stage): CP rows of BN values at pitch OP2
+  // (bf16) or OP4 (fp32)
+  static constexpr int OP2 = BN + 8;
+  static constexpr int OP4 = BN + 4;
+  static constexpr int STG_ELEMS = CP * OP4 * 2;  // bf16 units, fp32 case (the larger)
+  static constexpr int QP_RAW = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS) : Q_ELEMS + P_ELEMS;
+  static constexpr int QP_ELEMS = QP_RAW > STG_ELEMS ? QP_RAW : STG_ELEMS;
+  static constexpr bool STG_IN_P = !ALIAS_P && STG_ELEMS <= P_ELEMS;
+  // byte offsets (every region 16-byte aligned)
+  static constexpr int OFF_K = 2 * QP_ELEMS;
+  static constexpr int OFF_V = OFF_K + 2 * K_ELEMS;
+  static constexpr int OFF_POW = OFF_V + 2 * V_ELEMS;
+  static constexpr int OFF_ROWF = OFF_POW + ((CP + 2) * 4 + 15) / 16 * 16;
+  static constexpr int OFF_COLF = OFF_ROWF + 4 * CP;
+  static constexpr int BYTES = OFF_COLF + 4 * CP;
+  static_assert(OFF_K % 16 == 0 && OFF_V % 16 == 0 && OFF_POW % 16 == 0, "LDS regions must stay aligned");
+};
+
+// One chunk pass for workgroup slot xb of a launch (the whole body of the
+// kernels below).  SO (state only): the segment state pass -- only the state
+// update runs, from a zero state, and the segment's end state goes to
+// a.seg_state.
 template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO>
-__global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
+__device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, char* const smem) {
+  using Lds = ChunkLds<DK, BN, C, NT>;
   constexpr int NTHR = NW * 64;
   constexpr int NS = BN / (16 * NW);  // 16-column strips per wave
   static_assert(NS >= 1 && NS * 16 * NW == BN, "BN must split into 16-wide strips per wave");
   static_assert(DV % BN == 0, "DV must be a multiple of BN");
   static_assert(DK % 16 == 0 && C % 16 == 0, "dims must be multiples of 16");
   constexpr int NBLK = DV / BN;
-  constexpr int CP = (C + 31) / 32 * 32;    // chunk rows padded to the 32-deep k-step
-  constexpr int DKP = (DK + 31) / 32 * 32;  // DK padded likewise
-  constexpr int NTP = NT == 3 ? 3 : 2;      // terms of the masked P tile
+  constexpr int CP = Lds::CP;
+  constexpr int DKP = Lds::DKP;
+  constexpr int NTP = Lds::NTP;
   constexpr int NTS = NT == 3 ? 3 : 2;      // terms of state fragments
   constexpr int NTK = NT == 3 ? 3 : 2;      // terms of decay-scaled values
-  // LDS row pitches (elements), chosen from measured bank-conflict rates of
-  // each tile's access mix on gfx950: the query tile is read with 8-byte
-  // row reads, the key tile with 16-byte row reads and column reads, the P
-  // tile with 16-byte row reads, the value tile with column reads.
-  constexpr int PQ = DKP + 8;
-  constexpr int PK = DKP + 16;
-  constexpr int PVV = BN + 16;
-  constexpr int PP = pitch_p(CP);
+  constexpr int PQ = Lds::PQ;
+  constexpr int PK = Lds::PK;
+  constexpr int PVV = Lds::PVV;
+  constexpr int PP = Lds::PP;
   constexpr int DKT = DK / 16;  // 16-row tiles of the state
   constexpr int KSD = DKP / 32;  // 32-deep k-steps over DK
   constexpr int CT = CP / 16;    // 16-row tiles of a chunk
@@ -184,31 +236,20 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   constexpr int NPT = CT * (CT + 1) / 2;  // causal P tiles
   constexpr int MAXPT = (NPT + NW - 1) / NW;
   constexpr bool TIGHT = DK > 128;  // register-tight shape: pin the schedule
-
-  // LDS: query, key and value tiles plus the masked P tile.  When the four do
-  // not fit, P is held in registers until every read of the query tile is
-  // done and then written over it.
-  constexpr int Q_ELEMS = NT * CP * PQ;
-  constexpr int P_ELEMS = NTP * CP * PP;
-  constexpr int SEPARATE_BYTES = 2 * (Q_ELEMS + NT * CP * PK + NT * CP * PVV + P_ELEMS) + 4 * (3 * CP + 2);
-  constexpr bool ALIAS_P = SEPARATE_BYTES > 160 * 1024 - 512;
-  // output staging (see the store stage): CP rows of BN values at pitch OP2
-  // (bf16) or OP4 (fp32)
-  constexpr int OP2 = BN + 8;
-  constexpr int OP4 = BN + 4;
-  constexpr int STG_ELEMS = CP * OP4 * 2;  // bf16 units, fp32 case (the larger)
-  constexpr int QP_RAW = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS) : Q_ELEMS + P_ELEMS;
-  constexpr int QP_ELEMS = QP_RAW > STG_ELEMS ? QP_RAW : STG_ELEMS;
-  constexpr bool STG_IN_P = !ALIAS_P && STG_ELEMS <= P_ELEMS;
-  __shared__ __attribute__((aligned(16))) bf16_t sQP[QP_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16_t sK[NT * CP * PK];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[NT * CP * PVV];
-  __shared__ float sPow[CP + 2];
+  constexpr bool ALIAS_P = Lds::ALIAS_P;
+  constexpr int OP2 = Lds::OP2;
+  constexpr int OP4 = Lds::OP4;
+  constexpr bool STG_IN_P = Lds::STG_IN_P;
+  constexpr int Q_ELEMS = Lds::Q_ELEMS;
+  bf16_t* const sQP = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* const sK = reinterpret_cast<bf16_t*>(smem + Lds::OFF_K);
+  bf16_t* const sV = reinterpret_cast<bf16_t*>(smem + Lds::OFF_V);
+  float* const sPow = reinterpret_cast<float*>(smem + Lds::OFF_POW);
   // per-chunk factor tables for a chunk of L tokens: row factors (how the
   // entry state reaches row i) and column factors (how row j's key/value pair
   // reaches the exit state); zero beyond L
-  __shared__ __attribute__((aligned(16))) float sRowF[CP];
-  __shared__ __attribute__((aligned(16))) float sColF[CP];
+  float* const sRowF = reinterpret_cast<float*>(smem + Lds::OFF_ROWF);
+  float* const sColF = reinterpret_cast<float*>(smem + Lds::OFF_COLF);
   bf16_t* const sQ = sQP;
   bf16_t* const sP = ALIAS_P ? sQP : sQP + Q_ELEMS;
 
@@ -218,7 +259,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   // (b, h), so the tiles and segment states they share are served from that
   // XCD's L2.
   const int64_t BH = a.B * a.H;
-  const int xb = blockIdx.x;
   const int xcd = xb & 7;
   const int nseg = a.nseg;
   const int slot = xb >> 3;
@@ -279,7 +319,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int d = 16 * D + 4 * g + r;
+          const int d = state_row<DK>(D, g, r);
           const int n = col0 + 16 * s;
           float x = 0.0f;
           if (si) x = a.s_init_trans ? si[(int64_t)n * DK + d] : si[(int64_t)d * DV + n];
@@ -302,9 +342,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         for (int s = 0; s < NS; ++s)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            accS[D][s][r] = fmaf(dec, accS[D][s][r], E[(int64_t)(16 * D + 4 * g + r) * DV + col0 + 16 * s]);
+            accS[D][s][r] = fmaf(dec, accS[D][s][r], E[(int64_t)state_row<DK>(D, g, r) * DV + col0 + 16 * s]);
     }
   }
+
+  // The entry state has landed before the chunk loop starts.  (Without this
+  // explicit wait the compiler cannot prove it on every path into the loop
+  // and waits for all outstanding global loads -- including the next chunk's
+  // prefetch -- at the first use of the state in every iteration.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unchanged
 
   // writes 4 consecutive masked-P values of row i (cols 16 J + 4 g ..) as NTP planes
   auto put_p = [&](int i, int J, const f32x4& val) {
@@ -434,9 +480,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
     if constexpr (!SO) {
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
-      // State as the B operand of Q S: k-slot e of lane group g holds state
-      // row 32 ks + 16 (e / 4) + 4 g + (e % 4), which is what the accumulator
-      // layout already gives this lane; Q is read with the same permutation.
+      // State as the B operand of Q S: k-slot e of lane group g takes
+      // accumulator slot e % 4 of row tile 2 ks + e / 4, i.e. state row
+      // state_row(2 ks + e / 4, g, e % 4); Q is read at the same rows
+      // (32 ks + 8 g + e when DK is a multiple of 32).
       bf16x8 Sf[NS][NTS];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -456,7 +503,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
           const bf16_t* row = &sQ[p * CP * PQ + (16 * Iph + li) * PQ + 32 * ks];
-          Aq[p] = cat4(lds_read_b64(row + 4 * g), lds_read_b64(row + 16 + 4 * g));
+          if constexpr (DK % 32 == 0) Aq[p] = lds_read_b128(row + 8 * g);
+          else Aq[p] = cat4(lds_read_b64(row + 4 * g), lds_read_b64(row + 16 + 4 * g));
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma_split<NTS, NT>(accO[I][s], Sf[s], Aq);
@@ -560,7 +608,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
         bf16x8 Ak[NT];
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
-          const bf16_t* base = &sK[p * CP * PK + (32 * ks + 8 * g + (li >> 2)) * PK + 16 * D + 4 * (li & 3)];
+          // lane li supplies the 4-column group that lanes 4 (li & 3) .. + 3
+          // receive: their state rows (state_row) select the key columns
+          const int kc = DK % 32 == 0 ? 32 * (D >> 1) + 8 * (li & 3) + 4 * (D & 1) : 16 * D + 4 * (li & 3);
+          const bf16_t* base = &sK[p * CP * PK + (32 * ks + 8 * g + (li >> 2)) * PK + kc];
           Ak[p] = cat4(lds_read_tr(base), lds_read_tr(base + 4 * PK));
         }
 #pragma unroll
@@ -672,8 +723,25 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sf[(int64_t)(16 * D + 4 * g + r) * DV + col0 + 16 * s] = accS[D][s][r];
+        for (int r = 0; r < 4; ++r) sf[(int64_t)state_row<DK>(D, g, r) * DV + col0 + 16 * s] = accS[D][s][r];
   }
+}
+
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO>
+__global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT>::BYTES];
+  chunk_body<DK, DV, BN, NW, C, NT, REV, SO>(a, blockIdx.x, smem);
+}
+
+// Two independent passes of one shape in one launch, the first in forward
+// time and the second in reverse time: workgroups [0, nb0) run a0, the rest
+// run a1.  Each pass alone fills half the GPU.
+template <int DK, int DV, int BN, int NW, int C, int NT, bool SO>
+__global__ void __launch_bounds__(NW * 64) chunk_kernel_pair(ChunkArgs a0, ChunkArgs a1, int nb0) {
+  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT>::BYTES];
+  const int xb = blockIdx.x;
+  if (xb < nb0) chunk_body<DK, DV, BN, NW, C, NT, false, SO>(a0, xb, smem);
+  else chunk_body<DK, DV, BN, NW, C, NT, true, SO>(a1, xb - nb0, smem);
 }
 
 template <int DK, int DV, int BN, int NW, int C, int NT>
@@ -695,16 +763,36 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// column-block width per shape (must match launch_shape)
-static int block_cols(int dk, int dv) {
+template <int DK, int DV, int BN, int NW, int C, int NT>
+static hipError_t launch_pair(const ChunkArgs& a0, const ChunkArgs& a1, hipStream_t st) {
+  constexpr int NBLK = DV / BN;
+  const int64_t BH = a0.B * a0.H;
+  const int64_t groups = (BH + 7) / 8;
+  const int64_t nb = groups * 8 * NBLK * a0.nseg;  // per pass (both passes share dims)
+  if (nb <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(2 * nb)), block(NW * 64);
+  if (a0.nseg > 1) {
+    hipLaunchKernelGGL((chunk_kernel_pair<DK, DV, BN, NW, C, NT, true>), grid, block, 0, st, a0, a1, (int)nb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chunk_kernel_pair<DK, DV, BN, NW, C, NT, false>), grid, block, 0, st, a0, a1, (int)nb);
+  return hipGetLastError();
+}
+
+// column-block width per shape and chunk (must match launch_shape)
+static int block_cols(int dk, int dv, int chunk) {
   if (dk == 96 && dv == 192) return 96;
-  if (dk == 192 && dv == 96) return 48;
+  if (dk == 192 && dv == 96) return chunk <= 64 ? 96 : 48;
   return dv;  // the small shapes run all columns in one workgroup
 }
 
 int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk) {
   constexpr int64_t kTargetUnits = 256;  // one workgroup per compute unit of an MI355X
-  const int64_t units = B * H * (dv / block_cols(dk, dv));
+  const int nblk = dv / block_cols(dk, dv, chunk);
+  // the backward's two transposed passes share one launch when each has a
+  // single column block (launch_tiles)
+  const int64_t units = B * H * nblk * ((dk > dv && nblk == 1) ? 2 : 1);
   const int64_t nchunks = (T + chunk - 1) / chunk;
   if (units >= kTargetUnits || nchunks < 4) return 1;
   int64_t nseg = (kTargetUnits + units - 1) / units;
@@ -716,23 +804,46 @@ int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk) {
   return (int)((nchunks + seg_chunks - 1) / seg_chunks);
 }
 
+// One pass, or (a1 != null) two passes of the backward's transposed shape in
+// one launch (a forward-time, a1 reverse-time).
+template <int DK, int DV, int BN, int NW, int C, int NT>
+static hipError_t launch_tiles(const ChunkArgs& a, const ChunkArgs* a1, hipStream_t st) {
+  if constexpr (DK > DV && DV / BN == 1) {
+    if (a1) return launch_pair<DK, DV, BN, NW, C, NT>(a, *a1, st);
+  } else if constexpr (DK > DV) {
+    // narrow column blocks already fill the GPU: the two passes run in turn
+    if (a1) {
+      const hipError_t e = launch_one<DK, DV, BN, NW, C, NT>(a, st);
+      return e != hipSuccess ? e : launch_one<DK, DV, BN, NW, C, NT>(*a1, st);
+    }
+  } else {
+    if (a1) return hipErrorInvalidValue;
+  }
+  return launch_one<DK, DV, BN, NW, C, NT>(a, st);
+}
+
 // Tile shapes per (DK, DV): BN columns per workgroup, NW waves.
 template <int DK, int DV, int C, int NT>
-static hipError_t launch_shape(const ChunkArgs& a, hipStream_t st) {
-  if constexpr (DK == 96 && DV == 192) return launch_one<96, 192, 96, 6, C, NT>(a, st);
-  else if constexpr (DK == 192 && DV == 96) return launch_one<192, 96, 48, 3, C, NT>(a, st);
-  else if constexpr (DK == 16 && DV == 32) return launch_one<16, 32, 32, 2, C, NT>(a, st);
-  else if constexpr (DK == 32 && DV == 16) return launch_one<32, 16, 16, 1, C, NT>(a, st);
+static hipError_t launch_shape(const ChunkArgs& a, const ChunkArgs* a1, hipStream_t st) {
+  if constexpr (DK == 96 && DV == 192) return launch_tiles<96, 192, 96, 6, C, NT>(a, a1, st);
+  else if constexpr (DK == 192 && DV == 96) {
+    // all 96 columns on 6 waves (registers allow it up to 64-token chunks),
+    // else 48 columns on 3 waves with the wider register budget
+    if constexpr (C <= 64) return launch_tiles<192, 96, 96, 6, C, NT>(a, a1, st);
+    else return launch_tiles<192, 96, 48, 3, C, NT>(a, a1, st);
+  }
+  else if constexpr (DK == 16 && DV == 32) return launch_tiles<16, 32, 32, 2, C, NT>(a, a1, st);
+  else if constexpr (DK == 32 && DV == 16) return launch_tiles<32, 16, 16, 1, C, NT>(a, a1, st);
   else return hipErrorInvalidValue;
 }
 
 template <int DK, int DV, int NT>
-static hipError_t launch_chunks(int chunk, const ChunkArgs& a, hipStream_t st) {
+static hipError_t launch_chunks(int chunk, const ChunkArgs& a, const ChunkArgs* a1, hipStream_t st) {
   switch (chunk) {
-    case 16: return launch_shape<DK, DV, 16, NT>(a, st);
-    case 32: return launch_shape<DK, DV, 32, NT>(a, st);
-    case 64: return launch_shape<DK, DV, 64, NT>(a, st);
-    case 128: return launch_shape<DK, DV, 128, NT>(a, st);
+    case 16: return launch_shape<DK, DV, 16, NT>(a, a1, st);
+    case 32: return launch_shape<DK, DV, 32, NT>(a, a1, st);
+    case 64: return launch_shape<DK, DV, 64, NT>(a, a1, st);
+    case 128: return launch_shape<DK, DV, 128, NT>(a, a1, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -748,46 +859,58 @@ bool chunk_pass_supported(int dk, int dv, int chunk, int in_f32) {
   return chunk <= 32;
 }
 
-hipError_t launch_chunk_pass(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st) {
+static hipError_t launch_dispatch(int dk, int dv, int chunk, const ChunkArgs& a, const ChunkArgs* a1,
+                                  hipStream_t st) {
   if (!a.in_f32) {
-    if (dk == 96 && dv == 192) return launch_chunks<96, 192, 1>(chunk, a, st);
-    if (dk == 192 && dv == 96) return launch_chunks<192, 96, 1>(chunk, a, st);
-    if (dk == 16 && dv == 32) return launch_chunks<16, 32, 1>(chunk, a, st);
-    if (dk == 32 && dv == 16) return launch_chunks<32, 16, 1>(chunk, a, st);
+    if (dk == 96 && dv == 192) return launch_chunks<96, 192, 1>(chunk, a, a1, st);
+    if (dk == 192 && dv == 96) return launch_chunks<192, 96, 1>(chunk, a, a1, st);
+    if (dk == 16 && dv == 32) return launch_chunks<16, 32, 1>(chunk, a, a1, st);
+    if (dk == 32 && dv == 16) return launch_chunks<32, 16, 1>(chunk, a, a1, st);
   } else {
     if (dk == 16 && dv == 32) {
       switch (chunk) {
-        case 16: return launch_shape<16, 32, 16, 3>(a, st);
-        case 32: return launch_shape<16, 32, 32, 3>(a, st);
-        case 64: return launch_shape<16, 32, 64, 3>(a, st);
+        case 16: return launch_shape<16, 32, 16, 3>(a, a1, st);
+        case 32: return launch_shape<16, 32, 32, 3>(a, a1, st);
+        case 64: return launch_shape<16, 32, 64, 3>(a, a1, st);
         default: return hipErrorInvalidValue;
       }
     }
     if (dk == 32 && dv == 16) {
       switch (chunk) {
-        case 16: return launch_shape<32, 16, 16, 3>(a, st);
-        case 32: return launch_shape<32, 16, 32, 3>(a, st);
-        case 64: return launch_shape<32, 16, 64, 3>(a, st);
+        case 16: return launch_shape<32, 16, 16, 3>(a, a1, st);
+        case 32: return launch_shape<32, 16, 32, 3>(a, a1, st);
+        case 64: return launch_shape<32, 16, 64, 3>(a, a1, st);
         default: return hipErrorInvalidValue;
       }
     }
     if (dk == 96 && dv == 192) {
       switch (chunk) {
-        case 16: return launch_shape<96, 192, 16, 3>(a, st);
-        case 32: return launch_shape<96, 192, 32, 3>(a, st);
-        case 64: return launch_shape<96, 192, 64, 3>(a, st);
+        case 16: return launch_shape<96, 192, 16, 3>(a, a1, st);
+        case 32: return launch_shape<96, 192, 32, 3>(a, a1, st);
+        case 64: return launch_shape<96, 192, 64, 3>(a, a1, st);
         default: return hipErrorInvalidValue;
       }
     }
     if (dk == 192 && dv == 96) {
       switch (chunk) {
-        case 16: return launch_shape<192, 96, 16, 3>(a, st);
-        case 32: return launch_shape<192, 96, 32, 3>(a, st);
+        case 16: return launch_shape<192, 96, 16, 3>(a, a1, st);
+        case 32: return launch_shape<192, 96, 32, 3>(a, a1, st);
         default: return hipErrorInvalidValue;
       }
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_pass(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st) {
+  return launch_dispatch(dk, dv, chunk, a, nullptr, st);
+}
+
+hipError_t launch_chunk_pair(int dk, int dv, int chunk, const ChunkArgs& a0, const ChunkArgs& a1, hipStream_t st) {
+  if (dk <= dv || a0.reverse || !a1.reverse || a0.nseg != a1.nseg || a0.B != a1.B || a0.H != a1.H ||
+      a0.T != a1.T)
+    return hipErrorInvalidValue;
+  return launch_dispatch(dk, dv, chunk, a0, &a1, st);
 }
 
 }  // namespace gla

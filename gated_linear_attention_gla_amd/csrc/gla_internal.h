@@ -59,6 +59,10 @@ struct DecodeArgs {
 // One chunked pass; with a.nseg > 1 this is the segment state pass followed
 // by the full pass.
 hipError_t launch_chunk_pass(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st);
+// Two passes of a shape with dk > dv in one launch: a0 in forward time, a1 in
+// reverse time, same B, H, T and segments (each with its own seg_state).
+hipError_t launch_chunk_pair(int dk, int dv, int chunk, const ChunkArgs& a0, const ChunkArgs& a1,
+                             hipStream_t st);
 // Segments used for these dims (1 = no segment split) and the workspace bytes
 // they need: enough (b, h, column block, segment) units to fill the GPU.
 int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk);

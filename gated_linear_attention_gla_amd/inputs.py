@@ -95,6 +95,10 @@ CONFIGS = {
     "training": dict(cid=3, B=8, H=16, T=2048, dk=96, dv=192, chunk=128, dtype="bf16"),
     "long": dict(cid=4, B=1, H=16, T=65536, dk=96, dv=192, chunk=128, dtype="bf16"),
     "decode": dict(cid=5, N=1280, L=24, H=16, dk=96, dv=192, steps=64, dtype="bf16"),
+    # the training recipe under the page's own decay schedule (half-lives 1 to
+    # 2,048 tokens): head 0 has lambda = 1/2, so lambda^128 = 2^-128 is below
+    # the smallest normal fp32
+    "schedule": dict(cid=6, B=8, H=16, T=2048, dk=96, dv=192, chunk=128, dtype="bf16"),
 }
 
 
@@ -115,11 +119,14 @@ def make_chunk_inputs(name, B=None, T=None, with_grad=False, s0=None):
         out["v"] = normal(cid, TID["v"], (B, H, T, dv), sc, dt)
         out["lam"] = lambda_tiny(H)
         out["S0"] = None
-    elif name in ("laplace", "training"):
+    elif name in ("laplace", "training", "schedule"):
         out["q"] = normal(cid, TID["q"], (B, H, T, dk), 1.0, dt)
         out["k"] = normal(cid, TID["k"], (B, H, T, dk), 1.0 / math.sqrt(dk), dt)
         out["v"] = normal(cid, TID["v"], (B, H, T, dv), 1.0, dt)
-        out["lam"] = lambda_log_spaced(H, 0.9, 0.999)
+        if name == "schedule":
+            out["lam"] = lambda_half_life_schedule(H, 1.0, 2048.0)
+        else:
+            out["lam"] = lambda_log_spaced(H, 0.9, 0.999)
         out["S0"] = normal(cid, TID["S0"], (B, H, dk, dv), 0.01, "f32")
     elif name == "long":
         sc = 1.0 / math.sqrt(dk)
