@@ -269,6 +269,47 @@ def counted_traffic():
     return t.get("bwd_call_bytes")
 
 
+def bench_conv(gla, inputs, reps=50):
+    """Depthwise causal conv + SiLU in front of the mixer: the training batch
+    (B=8, T=2,048, D=3,072, bf16 in and out) and one decode step of 1,280
+    sequences (window state fp32, updated in place)."""
+    import numpy as np
+    import torch
+
+    c = inputs.make_conv_inputs()
+    B, T, D = c["cfg"]["B"], c["cfg"]["T"], c["cfg"]["D"]
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    x = d(c["x"]).to(torch.bfloat16)
+    w, bias = d(c["w"]), d(c["bias"])
+    y = torch.empty_like(x)
+    st = torch.empty((B, 3, D), dtype=torch.float32, device="cuda")
+    fwd = lambda: gla.conv1d_fwd(x, w, bias, None, y=y, state_out=st)
+    for _ in range(3):
+        fwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms = event_time_ms(fwd, reps, stream)
+    nbytes = B * T * D * (2 + 2) + B * 3 * D * 4 + D * 5 * 4
+    N = inputs.CONFIGS["decode"]["N"]
+    xs = torch.randn((N, D), device="cuda").to(torch.bfloat16)
+    win = torch.randn((N, 3, D), device="cuda")
+    ys = torch.empty_like(xs)
+    step = lambda: gla.conv1d_step_(xs, w, bias, win, y=ys)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    ms_s = event_time_ms(step, reps, stream)
+    sbytes = N * D * (2 + 2 + 2 * 3 * 4) + D * 5 * 4
+    return dict(
+        prefill=dict(workload=f"conv1d width 4 + SiLU, B={B} T={T} D={D}, bf16", ms=ms,
+                     tokens_per_s=B * T / (ms / 1e3), gbs=nbytes / (ms / 1e3) / 1e9,
+                     hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS),
+        decode_step=dict(workload=f"conv1d decode step, N={N} D={D}, bf16, fp32 window", ms=ms_s,
+                         gbs=sbytes / (ms_s / 1e3) / 1e9,
+                         hbm_frac=sbytes / (ms_s / 1e3) / 1e9 / HBM_PEAK_GBS),
+    )
+
+
 def cpu_baseline(inputs, min_seconds=5.0):
     """The fp64 oracle (token recurrence forward + two-sweep backward) on the
     training workload itself (B=8, 16 heads, 2,048 tokens; same recipe and
@@ -329,6 +370,10 @@ def main():
     log("bench: page decay schedule, training shape fwd+bwd")
     extra["schedule_fwd_bwd"] = bench_fwd_bwd_events(gla, inputs, "schedule", 20)
     log(f"  fwd {extra['schedule_fwd_bwd']['ms_fwd']:.3f} ms  bwd {extra['schedule_fwd_bwd']['ms_bwd']:.3f} ms")
+    log("bench: conv1d (prefill batch and decode step)")
+    extra["conv1d"] = bench_conv(gla, inputs)
+    log(f"  prefill {extra['conv1d']['prefill']['ms'] * 1e3:.1f} us  {extra['conv1d']['prefill']['gbs']:.0f} GB/s;"
+        f"  step {extra['conv1d']['decode_step']['ms'] * 1e3:.1f} us  {extra['conv1d']['decode_step']['gbs']:.0f} GB/s")
     dec = None
     if not args.no_decode:
         log("bench: decode")

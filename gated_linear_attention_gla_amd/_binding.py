@@ -97,6 +97,16 @@ def load_library(path=LIB_PATH):
         P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
         P(GlaTensor), vp,
     ]
+    lib.gla_conv1d_fwd.restype = ctypes.c_int
+    lib.gla_conv1d_fwd.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P(GlaTensor), vp, vp, vp,
+        P(GlaTensor), vp, vp,
+    ]
+    lib.gla_conv1d_step.restype = ctypes.c_int
+    lib.gla_conv1d_step.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, P(GlaTensor), vp, vp, vp, ctypes.c_int64,
+        P(GlaTensor), vp,
+    ]
     if path == LIB_PATH:
         _LIB = lib
     return lib
@@ -231,3 +241,70 @@ def decode_step_(q, k, v, lam, S, o=None, out_dtype=None):
     )
     _check(lib, st)
     return o
+
+
+CONV_WIDTH = 4
+
+
+def _act3(x):
+    """(b, t, d) activation tensor -> GlaTensor (stride_h unused)."""
+    if x.dim() != 3:
+        raise ValueError("expected a 3-D (b, t, d) tensor")
+    if x.numel() == 0:
+        return GlaTensor(None, _dtype_code(x.dtype), 0, 0, 0)
+    if x.shape[-1] > 1 and x.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    sb, st, _ = x.stride()
+    return GlaTensor(x.data_ptr(), _dtype_code(x.dtype), sb, 0, st)
+
+
+def _conv_w_ok(w, bias, D):
+    if w.dtype != torch.float32 or tuple(w.shape) != (D, CONV_WIDTH) or not w.is_contiguous():
+        raise ValueError(f"w must be a contiguous float32 tensor of shape {(D, CONV_WIDTH)}")
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (D,)):
+        raise ValueError(f"bias must be float32 of shape {(D,)}")
+
+
+def conv1d_fwd(x, w, bias=None, state_in=None, out_dtype=None, y=None, state_out=None,
+               return_state=True):
+    """y, state_out = conv1d_fwd(x, w, bias, state_in): depthwise causal conv
+    (width 4) + SiLU over x (B, T, D); state_in/state_out float32 (B, 3, D)."""
+    lib = load_library()
+    B, T, D = x.shape
+    _conv_w_ok(w, bias, D)
+    for name, st_ in (("state_in", state_in), ("state_out", state_out)):
+        if st_ is not None and (st_.dtype != torch.float32 or tuple(st_.shape) != (B, CONV_WIDTH - 1, D)
+                                or not st_.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 of shape {(B, CONV_WIDTH - 1, D)}")
+    if y is None:
+        y = torch.empty((B, T, D), dtype=out_dtype or x.dtype, device=x.device)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, CONV_WIDTH - 1, D), dtype=torch.float32, device=x.device)
+    tx, ty = _act3(x), _act3(y)
+    st = lib.gla_conv1d_fwd(B, T, D, ctypes.byref(tx), _ptr(w), _ptr(bias), _ptr(state_in),
+                            ctypes.byref(ty), _ptr(state_out), _stream())
+    _check(lib, st)
+    return y, state_out
+
+
+def conv1d_step_(x, w, bias, state, y=None, out_dtype=None):
+    """y = conv1d_step_(x, w, bias, state): one decode token per sequence;
+    x (N, D); state float32 (N, 3, D) view (windows dense per sequence), updated
+    in place; returns y (N, D)."""
+    lib = load_library()
+    N, D = x.shape
+    _conv_w_ok(w, bias, D)
+    if state.dtype != torch.float32 or tuple(state.shape) != (N, CONV_WIDTH - 1, D):
+        raise ValueError(f"state must be float32 of shape {(N, CONV_WIDTH - 1, D)}")
+    if state.stride()[1:] != (D, 1):
+        raise ValueError("each sequence's window must be dense in state")
+    if y is None:
+        y = torch.empty((N, D), dtype=out_dtype or x.dtype, device=x.device)
+    if x.stride(-1) != 1 or y.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    tx = GlaTensor(x.data_ptr(), _dtype_code(x.dtype), x.stride(0), 0, 0)
+    ty = GlaTensor(y.data_ptr(), _dtype_code(y.dtype), y.stride(0), 0, 0)
+    st = lib.gla_conv1d_step(N, D, ctypes.byref(tx), _ptr(w), _ptr(bias), _ptr(state), state.stride(0),
+                             ctypes.byref(ty), _stream())
+    _check(lib, st)
+    return y

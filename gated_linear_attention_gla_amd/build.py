@@ -16,7 +16,7 @@ REPO = os.path.dirname(PKG_DIR)
 BUILD_DIR = os.path.join(REPO, "_build", "gla")
 LIB_PATH = os.path.join(PKG_DIR, "libgla.so")
 
-SOURCES = ["gla_chunk.hip", "gla_decode.hip", "gla_api.cpp"]
+SOURCES = ["gla_chunk.hip", "gla_decode.hip", "gla_conv.hip", "gla_api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

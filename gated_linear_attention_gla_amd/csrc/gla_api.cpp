@@ -267,4 +267,81 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
   return GLA_OK;
 }
 
+// ---------------------------------------------------------------- convolution
+// [B, T, D] activation views for the convolution: stride_b over sequences,
+// stride_t over tokens, channels contiguous; stride_h is not used.
+static gla_status check_act(const gla_tensor* x, int64_t nb, int64_t nt, int64_t D) {
+  if (x->data == nullptr) return GLA_ERR_NULL;
+  if (!dtype_ok(x->dtype)) return GLA_ERR_DTYPE;
+  if (x->stride_b < 0 || x->stride_t < 0) return GLA_ERR_STRIDE;
+  const int64_t es = esize(x->dtype);
+  if (!aligned16(x->data)) return GLA_ERR_STRIDE;
+  if (nb > 1 && (x->stride_b * es) % 16 != 0) return GLA_ERR_STRIDE;
+  if (nt > 1 && ((x->stride_t * es) % 16 != 0 || x->stride_t < D)) return GLA_ERR_STRIDE;
+  return GLA_OK;
+}
+
+static bool conv_dims_ok(int64_t D) { return D >= 8 && D % 8 == 0 && D <= ((int64_t)1 << 24); }
+
+gla_status gla_conv1d_fwd(int64_t B, int64_t T, int64_t D, const gla_tensor* x, const float* w,
+                          const float* bias, const float* state_in, gla_tensor* y, float* state_out,
+                          void* stream) {
+  if (!x || !w || !y) return GLA_ERR_NULL;
+  if (B < 1 || T < 0 || !conv_dims_ok(D) || B > ((int64_t)1 << 24) || T > ((int64_t)1 << 40))
+    return GLA_ERR_SHAPE;
+  if (gla::conv_fwd_blocks(B, T, D) > (int64_t)0xFFFFFFFF) return GLA_ERR_SHAPE;
+  gla_status st;
+  if (T > 0) {
+    if ((st = check_act(x, B, T, D)) != GLA_OK) return st;
+    if ((st = check_act(y, B, T, D)) != GLA_OK) return st;
+  } else if (!dtype_ok(x->dtype) || !dtype_ok(y->dtype)) {
+    return GLA_ERR_DTYPE;
+  }
+  if (!aligned16(w) || !aligned16(bias) || !aligned16(state_in) || !aligned16(state_out))
+    return GLA_ERR_STRIDE;
+  const void* ins[] = {x->data, w, bias, state_in};
+  for (const void* p : ins)
+    if (same(y->data, p) || same(state_out, p)) return GLA_ERR_ALIAS;
+  if (same(y->data, state_out)) return GLA_ERR_ALIAS;
+
+  gla::ConvArgs a{};
+  a.x = x->data; a.sx_b = x->stride_b; a.sx_t = x->stride_t;
+  a.w = w; a.bias = bias; a.state_in = state_in;
+  a.y = y->data; a.sy_b = y->stride_b; a.sy_t = y->stride_t;
+  a.state_out = state_out;
+  a.B = B; a.T = T; a.D = D;
+  a.in_f32 = x->dtype == GLA_F32;
+  a.out_f32 = y->dtype == GLA_F32;
+  if (gla::launch_conv_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+gla_status gla_conv1d_step(int64_t N, int64_t D, const gla_tensor* x, const float* w, const float* bias,
+                           float* state, int64_t state_stride_n, gla_tensor* y, void* stream) {
+  if (!x || !w || !state || !y) return GLA_ERR_NULL;
+  if (N < 1 || !conv_dims_ok(D) || N > ((int64_t)1 << 30)) return GLA_ERR_SHAPE;
+  if (gla::conv_step_blocks(N, D) > (int64_t)0xFFFFFFFF) return GLA_ERR_SHAPE;
+  if (state_stride_n < (GLA_CONV_WIDTH - 1) * D) return GLA_ERR_SHAPE;
+  gla_status st;
+  if ((st = check_act(x, N, 1, D)) != GLA_OK) return st;
+  if ((st = check_act(y, N, 1, D)) != GLA_OK) return st;
+  if (!aligned16(w) || !aligned16(bias) || !aligned16(state) || (N > 1 && (state_stride_n * 4) % 16 != 0))
+    return GLA_ERR_STRIDE;
+  const void* ins[] = {x->data, w, bias};
+  for (const void* p : ins)
+    if (same(y->data, p) || same(state, p)) return GLA_ERR_ALIAS;
+  if (same(y->data, state)) return GLA_ERR_ALIAS;
+
+  gla::ConvStepArgs a{};
+  a.x = x->data; a.sx_n = x->stride_b;
+  a.w = w; a.bias = bias;
+  a.state = state; a.state_stride_n = state_stride_n;
+  a.y = y->data; a.sy_n = y->stride_b;
+  a.N = N; a.D = D;
+  a.in_f32 = x->dtype == GLA_F32;
+  a.out_f32 = y->dtype == GLA_F32;
+  if (gla::launch_conv_step(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
 }  // extern "C"

@@ -299,6 +299,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     const int d = rev ? (4 * g + r - li) : (li - 4 * g - r);
     dmask[r] = d >= 0 ? lam_pow_f32(lam, d) : 0.0f;
   }
+  // off-diagonal P-tile factors lam^(16 + e), e = li - 4 g - r (reverse:
+  // 4 g + r - li), e in [-15, 15]; read from the table once it is complete
+  float lp[4] = {0.f, 0.f, 0.f, 0.f};
 
   const char* qb = reinterpret_cast<const char*>(a.q);
   const char* kb = reinterpret_cast<const char*>(a.k);
@@ -415,6 +418,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     pfv.store(sV, tid);
     __syncthreads();  // sPow complete
     fill_factors(chunk_len(chunk_start(0)));
+    if constexpr (!TIGHT) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lp[r] = sPow[16 + (rev ? 4 * g + r - li : li - 4 * g - r)];
+    }
   }
 
   for (int64_t ci = 0; ci < nchunks; ++ci) {
@@ -429,46 +436,66 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     }
 
     // ---------------- stage 1: masked P tiles (causal half), P[i][j] row-major
+    // Each wave computes the tiles t = w, w + NW, ..., TP of them at a time so
+    // their LDS reads and MFMA chains overlap.  A slot past the last tile
+    // recomputes tile 0 and discards it, which keeps the code branch-free.
     f32x4 ptile[ALIAS_P ? MAXPT : 1];
     if constexpr (!SO) {
+      constexpr int TP = (TIGHT || MAXPT < 2) ? 1 : 2;
 #pragma unroll
-    for (int kt = 0; kt < MAXPT; ++kt) {
-      const int t = w + kt * NW;
-      if (NPT % NW == 0 || t < NPT) {
-        int Ip, Jp;
-        tile_of<CT>(t, Ip, Jp);
-        const int I = rev ? CT - 1 - Ip : Ip;
-        const int J = rev ? CT - 1 - Jp : Jp;
-        const int i = 16 * I + li;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kt0 = 0; kt0 < MAXPT; kt0 += TP) {
+        int Ia[TP], Ja[TP], da[TP];
+        bool ok[TP];
+        f32x4 acc[TP];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+          const int t = w + (kt0 + u) * NW;
+          ok[u] = (kt0 + u < MAXPT) && (NPT % NW == 0 || t < NPT);
+          int Ip, Jp;
+          tile_of<CT>(ok[u] ? t : 0, Ip, Jp);
+          Ia[u] = rev ? CT - 1 - Ip : Ip;
+          Ja[u] = rev ? CT - 1 - Jp : Jp;
+          da[u] = Ip - Jp;
+          acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-          bf16x8 A[NT], Bq[NT];
+          bf16x8 A[TP][NT], Bq[TP][NT];
 #pragma unroll
-          for (int p = 0; p < NT; ++p) {
-            A[p] = lds_read_b128(&sK[p * CP * PK + (16 * J + li) * PK + 32 * ks + 8 * g]);
-            Bq[p] = lds_read_b128(&sQ[p * CP * PQ + i * PQ + 32 * ks + 8 * g]);
+          for (int u = 0; u < TP; ++u)
+#pragma unroll
+            for (int p = 0; p < NT; ++p) {
+              A[u][p] = lds_read_b128(&sK[p * CP * PK + (16 * Ja[u] + li) * PK + 32 * ks + 8 * g]);
+              Bq[u][p] = lds_read_b128(&sQ[p * CP * PQ + (16 * Ia[u] + li) * PQ + 32 * ks + 8 * g]);
+            }
+#pragma unroll
+          for (int u = 0; u < TP; ++u) mma_split<NT, NT>(acc[u], A[u], Bq[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+          // acc[r] = q'_i . k'_j with i = 16 I + li, j = 16 J + 4 g + r.  The
+          // diagonal tile takes the per-lane mask; off the diagonal the
+          // exponent is 16 d + base -/+ r (d = Ip - Jp >= 1), formed as
+          // lam^(16 (d - 1)) (one value per tile) times lp[r] = lam^(16 + base -/+ r).
+          // (register-tight shapes read the whole exponent from the table)
+          if constexpr (TIGHT) {
+            const int base = 16 * da[u] + (rev ? 4 * g - li : li - 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[u][r] *= da[u] == 0 ? dmask[r] : sPow[da[u] == 0 ? 0 : (rev ? base + r : base - r)];
+          } else {
+            const float s16 = sPow[16 * (da[u] > 0 ? da[u] - 1 : 0)];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[u][r] *= da[u] == 0 ? dmask[r] : s16 * lp[r];
           }
-          mma_split<NT, NT>(acc, A, Bq);
+          if (ok[u]) {
+            if constexpr (ALIAS_P) ptile[(kt0 + u) < MAXPT ? kt0 + u : MAXPT - 1] = acc[u];
+            else put_p(16 * Ia[u] + li, Ja[u], acc[u]);
+          }
         }
-        // acc[r] = q'_i . k'_j with j = 16 J + 4 g + r; apply the decay mask.
-        // Off the diagonal every entry is inside the causal window and the
-        // exponent is 16 (Ip - Jp) + base -/+ r.
-        if (Ip == Jp) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] *= dmask[r];
-        } else {
-          const int base = 16 * (Ip - Jp) + (rev ? 4 * g - li : li - 4 * g);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] *= sPow[rev ? base + r : base - r];
-        }
-        if constexpr (ALIAS_P) ptile[kt] = acc;
-        else put_p(i, J, acc);
+        if constexpr (TIGHT) __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (TIGHT) __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (!ALIAS_P) put_zero_tiles();
-
+      if constexpr (!ALIAS_P) put_zero_tiles();
     }
 
     // ---------------- stage 2: O^T = S^T Q^T, rows scaled by the row factors

@@ -54,6 +54,34 @@ struct DecodeArgs {
   int in_f32;
 };
 
+// Depthwise causal convolution (width 4) + SiLU over [B][T][D] activations.
+struct ConvArgs {
+  const void* x;
+  int64_t sx_b, sx_t;      // element strides of x (channels contiguous)
+  const float* w;          // [D][4]
+  const float* bias;       // [D] or null
+  const float* state_in;   // [B][3][D] inputs before token 0, or null (zeros)
+  void* y;
+  int64_t sy_b, sy_t;
+  float* state_out;        // [B][3][D] last 3 inputs, or null
+  int64_t B, T, D;
+  int in_f32, out_f32;
+};
+
+// One decode token per sequence; the window is updated in place.
+struct ConvStepArgs {
+  const void* x;
+  int64_t sx_n;
+  const float* w;
+  const float* bias;
+  float* state;            // sequence n at state + n * state_stride_n, [3][D]
+  int64_t state_stride_n;
+  void* y;
+  int64_t sy_n;
+  int64_t N, D;
+  int in_f32, out_f32;
+};
+
 // Launchers return hipSuccess or the launch error.  They perform no
 // validation: the C-ABI layer checks every argument first.
 // One chunked pass; with a.nseg > 1 this is the segment state pass followed
@@ -69,5 +97,10 @@ int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk);
 bool chunk_pass_supported(int dk, int dv, int chunk, int in_f32);
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
 bool decode_supported(int dk, int dv);
+hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);
+hipError_t launch_conv_step(const ConvStepArgs& a, hipStream_t st);
+// one-dimensional grid sizes of the two convolution launches
+int64_t conv_fwd_blocks(int64_t B, int64_t T, int64_t D);
+int64_t conv_step_blocks(int64_t N, int64_t D);
 
 }  // namespace gla

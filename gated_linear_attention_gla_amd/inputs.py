@@ -99,7 +99,35 @@ CONFIGS = {
     # 2,048 tokens): head 0 has lambda = 1/2, so lambda^128 = 2^-128 is below
     # the smallest normal fp32
     "schedule": dict(cid=6, B=8, H=16, T=2048, dk=96, dv=192, chunk=128, dtype="bf16"),
+    # the convolution in front of the mixer: the training batch over the
+    # page's D = 3,072 residual channels
+    "conv": dict(cid=7, B=8, T=2048, D=3072, dtype="bf16"),
 }
+
+CONV_TID = {"x": 1, "w": 2, "bias": 3, "state": 4}
+
+
+def conv_inputs(seed, B, T, D, dtype="bf16", state=True, bias=True):
+    """Seeded convolution inputs: x ~ N(0, 1) (storage dtype), taps
+    w ~ N(0, 1/4) and bias ~ N(0, 1/100) in fp32, carried window
+    state ~ N(0, 1) fp32 (the inputs before token 0) or None."""
+    return dict(
+        x=normal(seed, CONV_TID["x"], (B, T, D), 1.0, dtype),
+        w=normal(seed, CONV_TID["w"], (D, 4), 0.5, "f32"),
+        bias=normal(seed, CONV_TID["bias"], (D,), 0.1, "f32") if bias else None,
+        state=normal(seed, CONV_TID["state"], (B, 3, D), 1.0, "f32") if state else None,
+    )
+
+
+def make_conv_inputs(B=None, T=None):
+    c = dict(CONFIGS["conv"])
+    if B is not None:
+        c["B"] = B
+    if T is not None:
+        c["T"] = T
+    out = conv_inputs(c["cid"], c["B"], c["T"], c["D"], c["dtype"], state=False)
+    out["cfg"] = c
+    return out
 
 
 def make_chunk_inputs(name, B=None, T=None, with_grad=False, s0=None):

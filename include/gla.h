@@ -151,6 +151,41 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
                            const gla_tensor* k, const gla_tensor* v, const float* lambda,
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Depthwise causal convolution (width GLA_CONV_WIDTH) + SiLU, the step in
+ * front of the mixer (page section "i14 and Laplace 3B architecture",
+ * paragraph "Normalization and convolution": every channel of the
+ * D = 3,072-wide residual stream is convolved causally over its last 4
+ * tokens and passed through SiLU; the window belongs to the per-sequence
+ * recurrent state).  For token t and channel c:
+ *   z = bias[c] + sum_{j<4} w[c][j] * x[t-3+j][c],   y[t][c] = z / (1 + exp(-z))
+ * so w[c][3] weights the current token.  Inputs before token 0 come from the
+ * carried window (oldest first), zero when it is NULL.  Arithmetic is fp32.
+ *   x, y      gla_tensor views of [B, T, D]: element (b, t, c) at
+ *             data + b*stride_b + t*stride_t + c (stride_h unused); bf16 or
+ *             fp32 each; 16-byte aligned rows, stride_t >= D
+ *   D         multiple of 8, >= 8
+ *   w         fp32 [D][4];  bias fp32 [D] or NULL
+ *   windows   fp32 [B][3][D], 16-byte aligned
+ * ------------------------------------------------------------------------ */
+#define GLA_CONV_WIDTH 4
+
+/* Prefill / training forward over T tokens (T = 0 copies state_in, or zeros,
+ * to state_out).  state_out (the last 3 inputs, ready for decode) may be
+ * NULL; it must not alias state_in. */
+gla_status gla_conv1d_fwd(int64_t B, int64_t T, int64_t D, const gla_tensor* x, const float* w,
+                          const float* bias, const float* state_in, gla_tensor* y, float* state_out,
+                          void* stream);
+
+/* One decode token for N sequences: y = SiLU(bias + w . [window, x]), then
+ * the window drops its oldest input and appends x, in place.
+ *   x, y   [N, D] views (stride_b steps n; stride_t unused)
+ *   state  sequence n's window at state + n*state_stride_n, [3][D] fp32;
+ *          state_stride_n >= 3*D (a per-sequence page may hold further
+ *          layers), a multiple of 4 when N > 1. */
+gla_status gla_conv1d_step(int64_t N, int64_t D, const gla_tensor* x, const float* w, const float* bias,
+                           float* state, int64_t state_stride_n, gla_tensor* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

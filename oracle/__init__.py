@@ -19,6 +19,7 @@ import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "gla_oracle.c")
+_SRCS = [_SRC, os.path.join(_DIR, "gla_conv_oracle.c")]
 _LIB_PATH = os.path.join(_DIR, "liboracle.so")
 _LIB = None
 
@@ -26,7 +27,7 @@ _LIB = None
 def build():
     """Compile liboracle.so with gcc (always rebuilds)."""
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", _SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", *_SRCS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -35,7 +36,7 @@ def build():
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(map(os.path.getmtime, _SRCS)):
             build()
         lib = ctypes.CDLL(_LIB_PATH)
         i64 = ctypes.c_int64
@@ -48,6 +49,8 @@ def _lib():
         lib.gla_oracle_bwd_bruteforce.argtypes = [i64] * 5 + [dp] * 11
         lib.gla_oracle_decode_step.argtypes = [i64] * 4 + [dp] * 6
         lib.gla_oracle_num_threads.restype = ctypes.c_int
+        lib.gla_oracle_conv1d.argtypes = [i64] * 4 + [dp] * 6
+        lib.gla_oracle_conv1d_step.argtypes = [i64] * 3 + [dp] * 5
         _LIB = lib
     return _LIB
 
@@ -146,3 +149,30 @@ def rel_err(got, ref):
     if den == 0.0:
         return float(num)
     return float(num / den)
+
+
+CONV_WIDTH = 4  # the page's convolution width
+
+
+def conv1d(x, w, bias=None, state_in=None):
+    """Depthwise causal conv + SiLU over x (B, T, D) with weights w (D, W):
+    returns (y, state_out) where state_out (B, W-1, D) holds the last W-1
+    inputs (see gla_conv_oracle.c)."""
+    x, w, bias, state_in = map(_f64, (x, w, bias, state_in))
+    B, T, D = x.shape
+    W = w.shape[1]
+    y = np.zeros((B, T, D))
+    st = np.zeros((B, W - 1, D))
+    _lib().gla_oracle_conv1d(B, T, D, W, _p(x), _p(w), _p(bias), _p(state_in), _p(y), _p(st))
+    return y, st
+
+
+def conv1d_step(x, w, bias, state):
+    """One decode token: x (N, D), state (N, W-1, D); returns (y, new_state)."""
+    x, w, bias = map(_f64, (x, w, bias))
+    st = np.array(state, dtype=np.float64, copy=True)
+    N, D = x.shape
+    W = w.shape[1]
+    y = np.zeros((N, D))
+    _lib().gla_oracle_conv1d_step(N, D, W, _p(x), _p(w), _p(bias), _p(st), _p(y))
+    return y, st

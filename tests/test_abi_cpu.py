@@ -233,3 +233,50 @@ def test_decode_validation(lib):
     assert dec(lib, 4, 2, 96, 192, q, k, v, o=o) == ALIAS
     q, k, v, o = dec_views()
     assert dec(lib, 4, 2, 96, 192, q, k, v, S=k.data, o=o) == ALIAS
+
+
+# ------------------------------------------------------------ convolution
+def conv_fwd(lib, B, T, D, x, y, w=0xA000, bias=None, sin=None, sout=None):
+    ref = lambda t: None if t is None else ctypes.byref(t)
+    return lib.gla_conv1d_fwd(B, T, D, ref(x), w, bias, sin, ref(y), sout, None)
+
+
+def act(ptr, T=16, D=64, dtype=gb.GLA_BF16):
+    return T_(ptr, dtype, T * D, D)
+
+
+def T_(ptr, dtype, sb, st):
+    return gb.GlaTensor(ptr, dtype, sb, 0, st)
+
+
+def test_conv_fwd_rejects_bad_arguments(lib):
+    x, y = act(0x100000), act(0x200000)
+    assert conv_fwd(lib, 2, 16, 64, None, y) == NULL
+    assert conv_fwd(lib, 2, 16, 64, x, y, w=None) == NULL
+    assert conv_fwd(lib, 0, 16, 64, x, y) == SHAPE
+    assert conv_fwd(lib, 2, -1, 64, x, y) == SHAPE
+    assert conv_fwd(lib, 2, 16, 60, x, y) == SHAPE           # D not a multiple of 8
+    assert conv_fwd(lib, 2, 16, 0, x, y) == SHAPE
+    assert conv_fwd(lib, 2, 16, 64, act(0x100008), y) == STRIDE   # misaligned base
+    assert conv_fwd(lib, 2, 16, 64, T_(0x100000, gb.GLA_BF16, 16 * 64, 32), y) == STRIDE  # stride_t < D
+    assert conv_fwd(lib, 2, 16, 64, x, y, w=0xA004) == STRIDE
+    assert conv_fwd(lib, 2, 16, 64, x, y, sin=0xB008) == STRIDE
+    assert conv_fwd(lib, 2, 16, 64, act(0x100000, dtype=7), y) == DTYPE
+    assert conv_fwd(lib, 2, 16, 64, x, act(0x100000)) == ALIAS       # y aliases x
+    assert conv_fwd(lib, 2, 16, 64, x, y, sin=0xB000, sout=0xB000) == ALIAS
+    assert conv_fwd(lib, 2, 16, 64, x, y, sout=0xA000) == ALIAS      # state_out aliases w
+
+
+def test_conv_step_rejects_bad_arguments(lib):
+    ref = ctypes.byref
+    x, y = T_(0x100000, gb.GLA_BF16, 64, 0), T_(0x200000, gb.GLA_BF16, 64, 0)
+    step = lambda N, D, xx, yy, state=0xC000, stride=192, w=0xA000: lib.gla_conv1d_step(
+        N, D, ref(xx), w, None, state, stride, ref(yy), None)
+    assert lib.gla_conv1d_step(4, 64, None, 0xA000, None, 0xC000, 192, ref(y), None) == NULL
+    assert step(4, 64, x, y, state=None) == NULL
+    assert step(0, 64, x, y) == SHAPE
+    assert step(4, 64, x, y, stride=191) == SHAPE            # window stride < 3 D
+    assert step(4, 64, x, y, stride=194) == STRIDE           # window rows misaligned
+    assert step(4, 64, x, y, state=0xC004) == STRIDE
+    assert step(4, 64, x, x) == ALIAS
+    assert step(4, 64, x, y, state=0x200000) == ALIAS
