@@ -310,6 +310,37 @@ def bench_conv(gla, inputs, reps=50):
     )
 
 
+def bench_varlen(gla, inputs, reps=20):
+    """Packed prefill of 64 prompts (lengths log-uniform in 16..4,096 tokens)
+    straight into their pages of a 1,280-sequence state pool."""
+    import numpy as np
+    import torch
+
+    c = inputs.CONFIGS["varlen"]
+    lengths = inputs.varlen_lengths(c["cid"], c["N"], c["min_len"], c["max_len"])
+    x = inputs.varlen_inputs(c["cid"], lengths, c["H"], c["dk"], c["dv"], num_slots=c["slots"])
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    q, k, v = (d(x[n]).to(torch.bfloat16) for n in ("q", "k", "v"))
+    lam = torch.tensor(inputs.lambda_log_spaced(c["H"], 0.95, 0.9999), dtype=torch.float32, device="cuda")
+    pool = d(x["pool"])[:, 0]
+    cu = torch.tensor(x["cu"], dtype=torch.int32, device="cuda")
+    slots = torch.tensor(x["slots"], dtype=torch.int32, device="cuda")
+    has = torch.tensor(x["has_state"], dtype=torch.int32, device="cuda")
+    total = int(lengths.sum())
+    o = torch.empty((total, c["H"], c["dv"]), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: gla.chunk_fwd_varlen(q, k, v, lam, cu, pool, slots, has, chunk=C, o=o)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ms = event_time_ms(fn, reps, torch.cuda.current_stream())
+    units = total * c["H"]
+    nbytes = units * FWD_BYTES + 2 * c["N"] * c["H"] * STATE_BYTES
+    return dict(workload=f"varlen prefill into the decode pool: {c['N']} prompts, {total} tokens "
+                         f"(16..4096 log-uniform), H={c['H']}, chunk={C}",
+                ms=ms, tokens_per_s=total / (ms / 1e3), gbs=nbytes / (ms / 1e3) / 1e9,
+                hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+
+
 def cpu_baseline(inputs, min_seconds=5.0):
     """The fp64 oracle (token recurrence forward + two-sweep backward) on the
     training workload itself (B=8, 16 heads, 2,048 tokens; same recipe and
@@ -370,6 +401,9 @@ def main():
     log("bench: page decay schedule, training shape fwd+bwd")
     extra["schedule_fwd_bwd"] = bench_fwd_bwd_events(gla, inputs, "schedule", 20)
     log(f"  fwd {extra['schedule_fwd_bwd']['ms_fwd']:.3f} ms  bwd {extra['schedule_fwd_bwd']['ms_bwd']:.3f} ms")
+    log("bench: varlen prefill into the decode pool")
+    extra["varlen_prefill"] = bench_varlen(gla, inputs)
+    log(f"  {extra['varlen_prefill']['ms']:.3f} ms  {extra['varlen_prefill']['tokens_per_s'] / 1e6:.2f} Mtok/s")
     log("bench: conv1d (prefill batch and decode step)")
     extra["conv1d"] = bench_conv(gla, inputs)
     log(f"  prefill {extra['conv1d']['prefill']['ms'] * 1e3:.1f} us  {extra['conv1d']['prefill']['gbs']:.0f} GB/s;"

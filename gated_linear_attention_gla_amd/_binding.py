@@ -97,6 +97,12 @@ def load_library(path=LIB_PATH):
         P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
         P(GlaTensor), vp,
     ]
+    lib.gla_chunk_fwd_varlen.restype = ctypes.c_int
+    lib.gla_chunk_fwd_varlen.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp, vp,
+        P(GlaTensor), vp,
+    ]
     lib.gla_conv1d_fwd.restype = ctypes.c_int
     lib.gla_conv1d_fwd.argtypes = [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P(GlaTensor), vp, vp, vp,
@@ -238,6 +244,49 @@ def decode_step_(q, k, v, lam, S, o=None, out_dtype=None):
     st = lib.gla_decode_step(
         N, H, dk, dv, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(lam),
         _ptr(S), S.stride(0), ctypes.byref(to), _stream(),
+    )
+    _check(lib, st)
+    return o
+
+
+def _packed(x):
+    """(t, h, d) packed tensor -> GlaTensor (stride_b unused)."""
+    if x.dim() != 3:
+        raise ValueError("expected a 3-D (t, h, d) tensor")
+    if x.numel() == 0:
+        return GlaTensor(None, _dtype_code(x.dtype), 0, 0, 0)
+    if x.shape[-1] > 1 and x.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    st, sh, _ = x.stride()
+    return GlaTensor(x.data_ptr(), _dtype_code(x.dtype), 0, sh, st)
+
+
+def chunk_fwd_varlen(q, k, v, lam, cu_seqlens, pool, slots=None, has_state=None, chunk=64,
+                     out_dtype=None, o=None):
+    """o = chunk_fwd_varlen(q, k, v, lam, cu_seqlens, pool): packed prefill of
+    N sequences (cu_seqlens int32 (N+1,) on the device) whose final states go
+    to their pages in pool (float32 (num_slots, H, dk, dv) view, heads dense),
+    in place.  slots / has_state: int32 (N,) or None."""
+    lib = load_library()
+    total_T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    N = cu_seqlens.shape[0] - 1
+    if pool.dtype != torch.float32 or pool.dim() != 4 or tuple(pool.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"pool must be float32 of shape (num_slots, {H}, {dk}, {dv})")
+    if pool.stride()[1:] != (dk * dv, dv, 1):
+        raise ValueError("each page's heads must be dense in pool")
+    for name, t in (("slots", slots), ("has_state", has_state)):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (N,)):
+            raise ValueError(f"{name} must be int32 of shape ({N},)")
+    if o is None:
+        o = torch.empty((total_T, H, dv), dtype=out_dtype or q.dtype, device=q.device)
+    tq, tk, tv, to = _packed(q), _packed(k), _packed(v), _packed(o)
+    st = lib.gla_chunk_fwd_varlen(
+        N, H, total_T, dk, dv, chunk, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+        _ptr(cu_seqlens), _ptr(lam), _ptr(pool), pool.shape[0], pool.stride(0), _ptr(slots),
+        _ptr(has_state), ctypes.byref(to), _stream(),
     )
     _check(lib, st)
     return o

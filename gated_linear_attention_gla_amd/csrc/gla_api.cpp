@@ -267,6 +267,53 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
   return GLA_OK;
 }
 
+gla_status gla_chunk_fwd_varlen(int64_t N, int64_t H, int64_t total_T, int64_t dk, int64_t dv,
+                                int64_t chunk, const gla_tensor* q, const gla_tensor* k,
+                                const gla_tensor* v, const int32_t* cu_seqlens, const float* lambda,
+                                float* pool, int64_t num_slots, int64_t pool_stride_n,
+                                const int32_t* slots, const int32_t* has_state, gla_tensor* o,
+                                void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens || !lambda || !pool) return GLA_ERR_NULL;
+  if (N < 1 || H < 1 || total_T < 0 || num_slots < 1 || N > ((int64_t)1 << 24) || H > ((int64_t)1 << 16) ||
+      N * H > ((int64_t)1 << 26) || total_T > ((int64_t)1 << 31) - 1 || num_slots > ((int64_t)1 << 31))
+    return GLA_ERR_SHAPE;
+  if (!dtype_ok(q->dtype) || !dtype_ok(o->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
+    return GLA_ERR_DTYPE;
+  const int in_f32 = q->dtype == GLA_F32;
+  if (!gla::chunk_pass_supported((int)dk, (int)dv, (int)chunk, in_f32)) return GLA_ERR_UNSUPPORTED;
+  if (pool_stride_n < H * dk * dv) return GLA_ERR_SHAPE;
+  gla_status st;
+  // packed [total_T, H, d] views: stride_t steps tokens, stride_h heads
+  const bool need = total_T > 0;
+  if ((st = check_view(q, 1, H, total_T, dk, chunk, need)) != GLA_OK) return st;
+  if ((st = check_view(k, 1, H, total_T, dk, chunk, need)) != GLA_OK) return st;
+  if ((st = check_view(v, 1, H, total_T, dv, chunk, need)) != GLA_OK) return st;
+  if ((st = check_view(o, 1, H, total_T, dv, chunk, need)) != GLA_OK) return st;
+  if (!aligned16(pool) || !aligned16(lambda) || (num_slots > 1 && (pool_stride_n * 4) % 16 != 0))
+    return GLA_ERR_STRIDE;
+  const void* ins[] = {q->data, k->data, v->data, lambda, cu_seqlens, slots, has_state};
+  for (const void* p : ins)
+    if (same(o->data, p) || same(pool, p)) return GLA_ERR_ALIAS;
+  if (same(o->data, pool)) return GLA_ERR_ALIAS;
+
+  const gla_dims dims{N, H, total_T, dk, dv, chunk};
+  ChunkArgs a = make_pass(&dims, q, k, v, lambda, nullptr, 0, nullptr, o, 0);
+  a.sq_b = a.sk_b = a.sv_b = a.so_b = 0;
+  a.nseg = 1;
+  a.seg_len = total_T > 0 ? total_T : 1;
+  a.seg_state = nullptr;
+  a.cu = cu_seqlens;
+  a.pool = pool;
+  a.pool_stride_n = pool_stride_n;
+  a.num_slots = num_slots;
+  a.slots = slots;
+  a.has_state = has_state;
+  if (gla::launch_chunk_pass((int)dk, (int)dv, (int)chunk, a, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
 // ---------------------------------------------------------------- convolution
 // [B, T, D] activation views for the convolution: stride_b over sequences,
 // stride_t over tokens, channels contiguous; stride_h is not used.

@@ -272,6 +272,26 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   const int64_t b = bh / a.H;
   const int64_t h = bh - b * a.H;
 
+  // this unit's tokens and state: the dense (b, h) layout, or a packed
+  // sequence with its state in a pool page
+  int64_t T = a.T, tbase = 0;
+  const float* s_init = a.s_init ? a.s_init + bh * (int64_t)DK * DV : nullptr;
+  float* s_final = a.s_final ? a.s_final + bh * (int64_t)DK * DV : nullptr;
+  if (a.cu) {
+    int64_t c0 = a.cu[b], c1 = a.cu[b + 1];
+    c0 = c0 < 0 ? 0 : (c0 > a.T ? a.T : c0);
+    c1 = c1 < c0 ? c0 : (c1 > a.T ? a.T : c1);
+    tbase = c0;
+    T = c1 - c0;
+  }
+  if (a.pool) {
+    const int64_t ps = a.slots ? a.slots[b] : b;
+    if (ps < 0 || ps >= a.num_slots) return;
+    float* page = a.pool + ps * a.pool_stride_n + h * (int64_t)DK * DV;
+    s_init = (a.has_state == nullptr || a.has_state[b] != 0) ? page : nullptr;
+    s_final = page;
+  }
+
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l = tid & 63;
@@ -307,15 +327,15 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   const char* kb = reinterpret_cast<const char*>(a.k);
   const char* vb = reinterpret_cast<const char*>(a.v);
   const int esz = a.in_f32 ? 4 : 2;
-  const int64_t q_off = b * a.sq_b + h * a.sq_h;
-  const int64_t k_off = b * a.sk_b + h * a.sk_h;
-  const int64_t v_off = b * a.sv_b + h * a.sv_h + (int64_t)nblk * BN;
+  const int64_t q_off = b * a.sq_b + h * a.sq_h + tbase * a.sq_t;
+  const int64_t k_off = b * a.sk_b + h * a.sk_h + tbase * a.sk_t;
+  const int64_t v_off = b * a.sv_b + h * a.sv_h + tbase * a.sv_t + (int64_t)nblk * BN;
   const int col0 = nblk * BN + w * NS * 16 + li;  // + 16 s: this lane's column in strip s
 
   // ---- state slice in accumulators: accS[D][s][r] = S[16 D + 4 g + r][col0 + 16 s]
   f32x4 accS[DKT][NS];
   {
-    const float* si = (!SO && a.s_init) ? a.s_init + bh * (int64_t)DK * DV : nullptr;
+    const float* si = SO ? nullptr : s_init;
 #pragma unroll
     for (int D = 0; D < DKT; ++D)
 #pragma unroll
@@ -329,7 +349,6 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           accS[D][s][r] = x;
         }
   }
-  const int64_t T = a.T;
   // The segments before this one (in walk order) enter through their end
   // states: S <- lam^len S + E, oldest first.
   if constexpr (!SO) {
@@ -703,7 +722,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       }
       __syncthreads();
       const int oes = f32o ? 4 : 2;
-      char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + t0 * a.so_t + nblk * BN) * oes;
+      char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + (tbase + t0) * a.so_t + nblk * BN) * oes;
       const uint32_t so_t = (uint32_t)a.so_t;
       const uint32_t nbytes = ((uint32_t)(L - 1) * so_t + BN) * oes;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)nbytes, 0x00020000);
@@ -742,7 +761,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // last segment in walk order returns the final state
   float* dst = nullptr;
   if constexpr (SO) dst = a.seg_state + (bh * nseg + seg) * (int64_t)DK * DV;
-  else if (a.s_final && seg == (REV ? 0 : nseg - 1)) dst = a.s_final + bh * (int64_t)DK * DV;
+  else if (s_final && seg == (REV ? 0 : nseg - 1)) dst = s_final;
   if (dst) {
     float* sf = dst;
 #pragma unroll

@@ -37,6 +37,18 @@ struct ChunkArgs {
   int nseg;
   int64_t seg_len;
   float* seg_state;
+  // Packed variable-length mode (prefill into the decode state pool).  With
+  // cu set, unit b covers tokens [cu[b], cu[b+1]) of the packed inputs
+  // (clamped to [0, T]; stride_b is then 0).  With pool set, unit (b, h)
+  // keeps its state in page slots[b] (or b) of the pool, at
+  // pool + slot * pool_stride_n + h * DK * DV: read at the start unless
+  // has_state[b] == 0, written back at the end; a slot outside
+  // [0, num_slots) skips the unit.  Neither mode splits segments.
+  const int32_t* cu;
+  float* pool;
+  int64_t pool_stride_n, num_slots;
+  const int32_t* slots;
+  const int32_t* has_state;
 };
 
 struct DecodeArgs {

@@ -106,6 +106,43 @@ CONFIGS = {
 
 CONV_TID = {"x": 1, "w": 2, "bias": 3, "state": 4}
 
+# packed prefill of a batch of prompts into the decode state pool: prompt
+# lengths log-uniform in [16, 4,096] tokens, pages for 1,280 sequences
+CONFIGS["varlen"] = dict(cid=8, N=64, H=16, dk=96, dv=192, min_len=16, max_len=4096, slots=1280,
+                         dtype="bf16")
+VARLEN_TID = {"len": 1, "q": 2, "k": 3, "v": 4, "slots": 5, "has": 6, "pool": 7}
+
+
+def varlen_lengths(seed, N, lo, hi):
+    """Seeded prompt lengths, log-uniform in [lo, hi] tokens."""
+    u = rng(seed, VARLEN_TID["len"]).uniform(math.log(lo), math.log(hi), size=N)
+    return np.floor(np.exp(u)).astype(np.int64)
+
+
+def varlen_inputs(seed, lengths, H, dk, dv, num_slots, dtype="bf16", pages=1, has_state=True,
+                  slots=True):
+    """Packed q, k, v [total_T, H, d] (~ N(0, 1/dk)), cu_seqlens, distinct
+    pool slots (a seeded choice among num_slots, or 0..N-1), per-sequence
+    has_state flags (seeded half/half, or all 1) and an initial pool
+    (num_slots, pages, H, dk, dv) ~ N(0, 0.01^2) fp32."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    N, total = len(lengths), int(lengths.sum())
+    sc = 1.0 / math.sqrt(dk)
+    cu = np.zeros(N + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    out = dict(
+        lengths=lengths, cu=cu,
+        q=normal(seed, VARLEN_TID["q"], (total, H, dk), sc, dtype),
+        k=normal(seed, VARLEN_TID["k"], (total, H, dk), sc, dtype),
+        v=normal(seed, VARLEN_TID["v"], (total, H, dv), sc, dtype),
+        slots=(rng(seed, VARLEN_TID["slots"]).choice(num_slots, size=N, replace=False) if slots
+               else np.arange(N)).astype(np.int64),
+        has_state=(rng(seed, VARLEN_TID["has"]).integers(0, 2, size=N) if has_state
+                   else np.ones(N, dtype=np.int64)),
+        pool=normal(seed, VARLEN_TID["pool"], (num_slots, pages, H, dk, dv), 0.01, "f32"),
+    )
+    return out
+
 
 def conv_inputs(seed, B, T, D, dtype="bf16", state=True, bias=True):
     """Seeded convolution inputs: x ~ N(0, 1) (storage dtype), taps

@@ -151,6 +151,35 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
                            const gla_tensor* k, const gla_tensor* v, const float* lambda,
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream);
 
+/* Variable-length batched prefill straight into the decode state pool (page
+ * sections "GLA mixer" and "Inference optimization on Trainium2": each
+ * sequence owns one fixed-size state page that prefill fills and every decode
+ * step then reads and writes).  N packed sequences, the forward of
+ * gla_chunk_fwd per sequence and head:
+ *   q, k [total_T, H, dk]; v, o [total_T, H, dv]  packed gla_tensor views:
+ *          element (t, h, d) at data + t*stride_t + h*stride_h + d
+ *          (stride_b unused); same dtype and layout rules as gla_chunk_fwd
+ *   cu_seqlens  device int32 [N+1]: sequence n is tokens [cu[n], cu[n+1]).
+ *          Entries are clamped to [0, total_T] and made non-decreasing on the
+ *          device, so bad offsets cannot reach outside the packed tensors.
+ *   pool   fp32 pages: sequence n's state for head h is the dense dk x dv
+ *          block at pool + slot*pool_stride_n + h*dk*dv, slot = slots[n]
+ *          (device int32 [N], or n when slots is NULL); pool_stride_n >=
+ *          H*dk*dv (a page may hold further layers), a multiple of 4 when
+ *          num_slots > 1.  Sequences whose slot is outside [0, num_slots)
+ *          are skipped (nothing read or written for them).
+ *   has_state  device int32 [N] or NULL: the sequence starts from its page's
+ *          state when nonzero (NULL: every sequence does), else from zero.
+ *          The final state is written back to the page (in place).
+ * No workspace.  Slots must be distinct (two sequences writing one page
+ * race). */
+gla_status gla_chunk_fwd_varlen(int64_t N, int64_t H, int64_t total_T, int64_t dk, int64_t dv,
+                                int64_t chunk, const gla_tensor* q, const gla_tensor* k,
+                                const gla_tensor* v, const int32_t* cu_seqlens, const float* lambda,
+                                float* pool, int64_t num_slots, int64_t pool_stride_n,
+                                const int32_t* slots, const int32_t* has_state, gla_tensor* o,
+                                void* stream);
+
 /* ------------------------------------------------------------------------
  * Depthwise causal convolution (width GLA_CONV_WIDTH) + SiLU, the step in
  * front of the mixer (page section "i14 and Laplace 3B architecture",

@@ -280,3 +280,31 @@ def test_conv_step_rejects_bad_arguments(lib):
     assert step(4, 64, x, y, state=0xC004) == STRIDE
     assert step(4, 64, x, x) == ALIAS
     assert step(4, 64, x, y, state=0x200000) == ALIAS
+
+
+# ------------------------------------------------------------ varlen prefill
+def test_varlen_rejects_bad_arguments(lib):
+    ref = ctypes.byref
+
+    def call(N=4, H=2, Tt=100, dk=96, dv=192, chunk=64, q=0x100000, o=0x400000, cu=0x700000, lam=0x9000,
+             pool=0x800000, slots_n=8, pstride=2 * 96 * 192, dtype=gb.GLA_BF16):
+        tq = gb.GlaTensor(q, dtype, 0, dk, H * dk)
+        tk = gb.GlaTensor(0x200000, dtype, 0, dk, H * dk)
+        tv = gb.GlaTensor(0x300000, dtype, 0, dv, H * dv)
+        to = gb.GlaTensor(o, dtype, 0, dv, H * dv)
+        return lib.gla_chunk_fwd_varlen(N, H, Tt, dk, dv, chunk, ref(tq), ref(tk), ref(tv), cu, lam, pool,
+                                        slots_n, pstride, None, None, ref(to), None)
+
+    assert call(cu=None) == NULL
+    assert call(pool=None) == NULL
+    assert call(N=0) == SHAPE
+    assert call(Tt=-1) == SHAPE
+    assert call(slots_n=0) == SHAPE
+    assert call(pstride=2 * 96 * 192 - 1) == SHAPE
+    assert call(dk=64) == UNSUP
+    assert call(chunk=48) == UNSUP
+    assert call(pool=0x800008) == STRIDE
+    assert call(pstride=2 * 96 * 192 + 2) == STRIDE
+    assert call(o=0x100000) == ALIAS
+    assert call(pool=0x400000) == ALIAS
+    assert call(dtype=9) == DTYPE
