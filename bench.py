@@ -310,6 +310,32 @@ def bench_conv(gla, inputs, reps=50):
     )
 
 
+def bench_fused(gla, inputs, reps=20):
+    """Training-shape forward with the output epilogue fused into the store
+    (self-augmentation, Head RMSNorm, SiLU gate over a bf16 gate stream)."""
+    import numpy as np
+    import torch
+
+    x = inputs.make_chunk_inputs("training")
+    cfg = x["cfg"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    e = inputs.epilogue_inputs(750, B, H, T, DK, DV, "bf16", aug_scale=0.1)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    q, k, v, g = (d(t).to(torch.bfloat16) for t in (x["q"], x["k"], x["v"], e["g"]))
+    lam, S0, aug, gamma = d(x["lam"]), d(x["S0"]), d(e["aug"]), d(e["gamma"])
+    y = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
+    fn = lambda: gla.chunk_fwd_fused(q, k, v, lam, g, aug, gamma, 1e-6, S0, chunk=C, y=y, S_T=S_T)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ms = event_time_ms(fn, reps, torch.cuda.current_stream())
+    nbytes = B * H * T * (FWD_BYTES + 2 * DV) + 2 * B * H * STATE_BYTES
+    return dict(workload=f"fwd + fused output epilogue, B={B} H={H} T={T} chunk={C}, bf16 q/k/v/g/y",
+                ms=ms, tokens_per_s=B * T / (ms / 1e3), gbs=nbytes / (ms / 1e3) / 1e9,
+                hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+
+
 def bench_varlen(gla, inputs, reps=20):
     """Packed prefill of 64 prompts (lengths log-uniform in 16..4,096 tokens)
     straight into their pages of a 1,280-sequence state pool."""
@@ -401,6 +427,9 @@ def main():
     log("bench: page decay schedule, training shape fwd+bwd")
     extra["schedule_fwd_bwd"] = bench_fwd_bwd_events(gla, inputs, "schedule", 20)
     log(f"  fwd {extra['schedule_fwd_bwd']['ms_fwd']:.3f} ms  bwd {extra['schedule_fwd_bwd']['ms_bwd']:.3f} ms")
+    log("bench: fwd with the fused output epilogue")
+    extra["fused_epilogue_fwd"] = bench_fused(gla, inputs)
+    log(f"  {extra['fused_epilogue_fwd']['ms']:.3f} ms")
     log("bench: varlen prefill into the decode pool")
     extra["varlen_prefill"] = bench_varlen(gla, inputs)
     log(f"  {extra['varlen_prefill']['ms']:.3f} ms  {extra['varlen_prefill']['tokens_per_s'] / 1e6:.2f} Mtok/s")

@@ -97,6 +97,13 @@ def load_library(path=LIB_PATH):
         P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
         P(GlaTensor), vp,
     ]
+    lib.gla_chunk_fwd_fused_workspace.restype = ctypes.c_size_t
+    lib.gla_chunk_fwd_fused_workspace.argtypes = [P(GlaDims)]
+    lib.gla_chunk_fwd_fused.restype = ctypes.c_int
+    lib.gla_chunk_fwd_fused.argtypes = [
+        P(GlaDims), P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, P(GlaTensor), vp, vp,
+        ctypes.c_float, P(GlaTensor), vp, vp, ctypes.c_size_t, vp,
+    ]
     lib.gla_chunk_fwd_varlen.restype = ctypes.c_int
     lib.gla_chunk_fwd_varlen.argtypes = [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -247,6 +254,36 @@ def decode_step_(q, k, v, lam, S, o=None, out_dtype=None):
     )
     _check(lib, st)
     return o
+
+
+def chunk_fwd_fused(q, k, v, lam, g, aug, gamma, eps=1e-6, S0=None, chunk=64, out_dtype=None, y=None,
+                    S_T=None, return_state=True):
+    """y, S_T = chunk_fwd_fused(q, k, v, lam, g, aug, gamma, eps, S0): chunked
+    forward with the output epilogue (self-augmentation, Head RMSNorm, SiLU
+    gate) fused into the store.  g: (B, H, T, dv) view of the gate stream;
+    aug float32 (H, dk); gamma float32 (H, dv)."""
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _state_ok(S0, B, H, dk, dv, "S0")
+    for name, t, shp in (("aug", aug, (H, dk)), ("gamma", gamma, (H, dv))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shp}")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=out_dtype or q.dtype, device=q.device)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    dims = GlaDims(B, H, T, dk, dv, chunk)
+    nws = lib.gla_chunk_fwd_fused_workspace(ctypes.byref(dims))
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+    tq, tk, tv, tg, ty = _view4(q), _view4(k), _view4(v), _view4(g), _view4(y)
+    st = lib.gla_chunk_fwd_fused(
+        ctypes.byref(dims), ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(lam), _ptr(S0),
+        ctypes.byref(tg), _ptr(aug), _ptr(gamma), ctypes.c_float(eps), ctypes.byref(ty), _ptr(S_T),
+        _ptr(ws), nws, _stream(),
+    )
+    _check(lib, st)
+    return y, S_T
 
 
 def _packed(x):

@@ -267,6 +267,58 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
   return GLA_OK;
 }
 
+size_t gla_chunk_fwd_fused_workspace(const gla_dims* dims) {
+  if (!dims || check_dims(dims) != GLA_OK) return 0;
+  const int nseg = gla::chunk_segments_fused(dims->B, dims->H, dims->T, (int)dims->chunk);
+  if (nseg <= 1) return 0;
+  return (size_t)dims->B * dims->H * nseg * dims->dk * dims->dv * sizeof(float);
+}
+
+gla_status gla_chunk_fwd_fused(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                               const gla_tensor* v, const float* lambda, const float* S0,
+                               const gla_tensor* g, const float* aug, const float* gamma, float eps,
+                               gla_tensor* y, float* S_T, void* ws, size_t ws_bytes, void* stream) {
+  if (!dims || !q || !k || !v || !g || !y || !lambda || !aug || !gamma) return GLA_ERR_NULL;
+  gla_status st = check_dims(dims);
+  if (st != GLA_OK) return st;
+  if (!(eps >= 0.0f) || eps > 1e30f) return GLA_ERR_SHAPE;
+  const int64_t B = dims->B, H = dims->H, T = dims->T;
+  if (!dtype_ok(q->dtype) || !dtype_ok(y->dtype) || k->dtype != q->dtype || v->dtype != q->dtype ||
+      g->dtype != q->dtype)
+    return GLA_ERR_DTYPE;
+  const int in_f32 = q->dtype == GLA_F32;
+  if (!gla::chunk_fused_supported((int)dims->dk, (int)dims->dv, (int)dims->chunk, in_f32))
+    return GLA_ERR_UNSUPPORTED;
+  const bool need = T > 0;
+  const int64_t DK = dims->dk, DV = dims->dv, C = dims->chunk;
+  if ((st = check_view(q, B, H, T, DK, C, need)) != GLA_OK) return st;
+  if ((st = check_view(k, B, H, T, DK, C, need)) != GLA_OK) return st;
+  if ((st = check_view(v, B, H, T, DV, C, need)) != GLA_OK) return st;
+  if ((st = check_view(g, B, H, T, DV, C, need)) != GLA_OK) return st;
+  if ((st = check_view(y, B, H, T, DV, C, need)) != GLA_OK) return st;
+  if (!aligned16(S0) || !aligned16(S_T) || !aligned16(lambda) || !aligned16(aug) || !aligned16(gamma))
+    return GLA_ERR_STRIDE;
+  const void* ins[] = {q->data, k->data, v->data, g->data, lambda, S0, aug, gamma};
+  for (const void* p : ins)
+    if (same(y->data, p) || same(S_T, p)) return GLA_ERR_ALIAS;
+  if (same(y->data, S_T)) return GLA_ERR_ALIAS;
+  const size_t need_ws = gla_chunk_fwd_fused_workspace(dims);
+  if (ws_bytes < need_ws || (need_ws > 0 && (ws == nullptr || !aligned16(ws)))) return GLA_ERR_WORKSPACE;
+
+  ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, y, 0);
+  a.nseg = gla::chunk_segments_fused(B, H, T, (int)C);
+  a.seg_len = a.nseg > 1 ? seg_len_for(T, C, a.nseg) : (T > 0 ? T : 1);
+  a.seg_state = a.nseg > 1 ? static_cast<float*>(ws) : nullptr;
+  a.gz = g->data;
+  a.sg_b = g->stride_b; a.sg_h = g->stride_h; a.sg_t = g->stride_t;
+  a.aug = aug;
+  a.gamma = gamma;
+  a.eps = eps;
+  if (gla::launch_chunk_fused((int)DK, (int)DV, (int)C, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
 gla_status gla_chunk_fwd_varlen(int64_t N, int64_t H, int64_t total_T, int64_t dk, int64_t dv,
                                 int64_t chunk, const gla_tensor* q, const gla_tensor* k,
                                 const gla_tensor* v, const int32_t* cu_seqlens, const float* lambda,

@@ -168,7 +168,7 @@ __device__ __forceinline__ int state_row(int D, int g, int r) {
 
 // LDS layout of one chunk pass: query, key and value tiles plus the masked P
 // tile (bf16 planes), the lam^n table and the per-chunk factor tables.
-template <int DK, int BN, int C, int NT>
+template <int DK, int BN, int C, int NT, int NW = 1, bool EPI = false>
 struct ChunkLds {
   static constexpr int CP = (C + 31) / 32 * 32;    // chunk rows padded to the 32-deep k-step
   static constexpr int DKP = (DK + 31) / 32 * 32;  // DK padded likewise
@@ -203,7 +203,14 @@ struct ChunkLds {
   static constexpr int OFF_POW = OFF_V + 2 * V_ELEMS;
   static constexpr int OFF_ROWF = OFF_POW + ((CP + 2) * 4 + 15) / 16 * 16;
   static constexpr int OFF_COLF = OFF_ROWF + 4 * CP;
-  static constexpr int BYTES = OFF_COLF + 4 * CP;
+  // output epilogue: gate partial dots [CP][DK/8], per-row partial sums of
+  // squares [CP][NWP], the gates [CP] and the per-head channel scales [DK]
+  static constexpr int NWP = (NW + 3) / 4 * 4;
+  static constexpr int OFF_GP = OFF_COLF + 4 * CP;
+  static constexpr int OFF_SQ = OFF_GP + (EPI ? 4 * CP * (DK / 8) : 0);
+  static constexpr int OFF_GATE = OFF_SQ + (EPI ? 4 * CP * NWP : 0);
+  static constexpr int OFF_AUG = OFF_GATE + (EPI ? 4 * CP : 0);
+  static constexpr int BYTES = OFF_AUG + (EPI ? 4 * DK : 0);
   static_assert(OFF_K % 16 == 0 && OFF_V % 16 == 0 && OFF_POW % 16 == 0, "LDS regions must stay aligned");
 };
 
@@ -211,9 +218,9 @@ struct ChunkLds {
 // kernels below).  SO (state only): the segment state pass -- only the state
 // update runs, from a zero state, and the segment's end state goes to
 // a.seg_state.
-template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO>
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false>
 __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, char* const smem) {
-  using Lds = ChunkLds<DK, BN, C, NT>;
+  using Lds = ChunkLds<DK, BN, C, NT, NW, EPI>;
   constexpr int NTHR = NW * 64;
   constexpr int NS = BN / (16 * NW);  // 16-column strips per wave
   static_assert(NS >= 1 && NS * 16 * NW == BN, "BN must split into 16-wide strips per wave");
@@ -250,6 +257,14 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // reaches the exit state); zero beyond L
   float* const sRowF = reinterpret_cast<float*>(smem + Lds::OFF_ROWF);
   float* const sColF = reinterpret_cast<float*>(smem + Lds::OFF_COLF);
+  // output epilogue (EPI): the workgroup owns every column of its head
+  static_assert(!EPI || (NBLK == 1 && !REV && !Lds::ALIAS_P), "the epilogue needs whole heads, forward time");
+  constexpr int NWP = Lds::NWP;
+  constexpr int PPR = DK / 8;  // 8-element parts of a row in the gate dot
+  float* const sGP = reinterpret_cast<float*>(smem + Lds::OFF_GP);
+  float* const sSq = reinterpret_cast<float*>(smem + Lds::OFF_SQ);
+  float* const sGate = reinterpret_cast<float*>(smem + Lds::OFF_GATE);
+  float* const sAug = reinterpret_cast<float*>(smem + Lds::OFF_AUG);
   bf16_t* const sQ = sQP;
   bf16_t* const sP = ALIAS_P ? sQP : sQP + Q_ELEMS;
 
@@ -301,6 +316,17 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 
   const float lam = a.lam[h];
   for (int n = tid; n <= CP + 1; n += NTHR) sPow[n] = lam_pow_f32(lam, n);
+  // epilogue: the head's channel scales, zeroed row-sum padding, and this
+  // lane's RMSNorm weights (output columns (w NS + s) 16 + 4 g + r)
+  float gam[NS][4];
+  if constexpr (EPI && !SO) {
+    for (int n = tid; n < DK; n += NTHR) sAug[n] = a.aug[h * DK + n];
+    for (int n = tid; n < CP * NWP; n += NTHR) sSq[n] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gam[s][r] = a.gamma[h * DV + (w * NS + s) * 16 + 4 * g + r];
+  }
   // (reads sPow: every call site is preceded by a barrier after sPow is filled)
   auto fill_factors = [&](int Lc) {
     for (int n = tid; n < CP; n += NTHR) {
@@ -596,7 +622,39 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       }
       put_zero_tiles();
     }
+    if constexpr (EPI && !SO) {
+      // self-augmentation gate: partial dots q_i . (aug * k_i) over 8 channels
+      for (int u = tid; u < CP * PPR; u += NTHR) {
+        const int row = u / PPR;
+        const int part = u - row * PPR;
+        bf16x8 qp[NT], kp[NT];
+#pragma unroll
+        for (int p = 0; p < NT; ++p) {
+          qp[p] = lds_read_b128(&sQ[p * CP * PQ + row * PQ + part * 8]);
+          kp[p] = lds_read_b128(&sK[p * CP * PK + row * PK + part * 8]);
+        }
+        float sacc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float qe = 0.0f, ke = 0.0f;
+#pragma unroll
+          for (int p = 0; p < NT; ++p) {
+            qe += bf16v_to_f32(qp[p][e]);
+            ke += bf16v_to_f32(kp[p][e]);
+          }
+          sacc = fmaf(qe * sAug[part * 8 + e], ke, sacc);
+        }
+        sGP[u] = sacc;
+      }
+    }
     if constexpr (!SO) __syncthreads();  // P complete
+    if constexpr (EPI && !SO) {
+      for (int row = tid; row < CP; row += NTHR) {
+        float sdot = 0.0f;
+        for (int part = 0; part < PPR; ++part) sdot += sGP[row * PPR + part];
+        sGate[row] = 1.0f / (1.0f + expf(-sdot));
+      }
+    }
 
     // ---------------- stage 3: O += P V ; stage 4: S += (colfac K)^T V
     // Logical k-steps kl and row tiles I keep the causal structure static:
@@ -678,6 +736,25 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       for (int kl = 0; kl < KSC; ++kl) kstep(kl);
     }
 
+    // epilogue: this lane's values v[16 I + li][(w NS + s) 16 + 4 g + r],
+    // read while the value tile is still in LDS
+    float vreg[EPI ? CT : 1][NS][4];
+    if constexpr (EPI && !SO) {
+#pragma unroll
+      for (int I = 0; I < CT; ++I)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vreg[I][s][r] = 0.0f;
+#pragma unroll
+          for (int p = 0; p < NT; ++p) {
+            const bf16x4 t = lds_read_b64(&sV[p * CP * PVV + (16 * I + li) * PVV + (w * NS + s) * 16 + 4 * g]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vreg[I][s][r] += bf16v_to_f32(t[r]);
+          }
+        }
+    }
+
     // ---------------- next chunk's tiles -> LDS; store O (rows < L)
     // O is staged through LDS so that the global stores are 16-byte,
     // row-contiguous and coalesced.  accO holds O^T tiles: lane (g, li) has
@@ -699,7 +776,103 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     if constexpr (STG_IN_P) {
       if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
     }
-    if constexpr (!SO) {
+    if constexpr (EPI && !SO) {
+      // o' = o + gate v, then per-row sums of squares over this wave's columns
+#pragma unroll
+      for (int I = 0; I < CT; ++I) {
+        const int row = 16 * I + li;
+        const float gt = sGate[row];
+        float ss = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            accO[I][s][r] = fmaf(gt, vreg[I][s][r], accO[I][s][r]);
+            ss = fmaf(accO[I][s][r], accO[I][s][r], ss);
+          }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        if (g == 0) sSq[row * NWP + w] = ss;
+      }
+      __syncthreads();  // row sums complete
+      // Head RMSNorm and its weight; staged in fp32
+      float* st4 = reinterpret_cast<float*>(STG_IN_P ? sP : sQP);
+#pragma unroll
+      for (int I = 0; I < CT; ++I) {
+        const int row = 16 * I + li;
+        float tot = 0.0f;
+#pragma unroll
+        for (int v4 = 0; v4 < NWP; v4 += 4) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(&sSq[row * NWP + v4]);
+          tot += (t[0] + t[1]) + (t[2] + t[3]);
+        }
+        const float rstd = 1.0f / sqrtf(tot * (1.0f / DV) + a.eps);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          f32x4 y;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = accO[I][s][r] * rstd * gam[s][r];
+          *reinterpret_cast<f32x4*>(&st4[row * OP4 + (w * NS + s) * 16 + 4 * g]) = y;
+        }
+      }
+      __syncthreads();
+      // y * SiLU(gate stream): 8 columns per thread, coalesced 16-byte rows
+      const int oes = a.o_f32 ? 4 : 2;
+      const int ges = a.in_f32 ? 4 : 2;
+      char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + (tbase + t0) * a.so_t) * oes;
+      const char* gbase =
+          reinterpret_cast<const char*>(a.gz) + (b * a.sg_b + h * a.sg_h + (tbase + t0) * a.sg_t) * ges;
+      const __amdgpu_buffer_rsrc_t rso = __builtin_amdgcn_make_buffer_rsrc(
+          obase, (short)0, (int)(((uint32_t)(L - 1) * (uint32_t)a.so_t + BN) * oes), 0x00020000);
+      const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(gbase), (short)0, (int)(((uint32_t)(L - 1) * (uint32_t)a.sg_t + BN) * ges), 0x00020000);
+      constexpr int VPR8 = BN / 8;
+      static_assert(NTHR % VPR8 == 0, "threads must cover whole rows");
+      constexpr int RPJ8 = NTHR / VPR8;
+      const int row0 = tid / VPR8;
+      const int cv = tid - row0 * VPR8;
+#pragma unroll
+      for (int j = 0; j < (CP + RPJ8 - 1) / RPJ8; ++j) {
+        const int row = row0 + j * RPJ8;
+        if (CP % RPJ8 == 0 || row < CP) {
+          const f32x4 y0 = *reinterpret_cast<const f32x4*>(&st4[row * OP4 + cv * 8]);
+          const f32x4 y1 = *reinterpret_cast<const f32x4*>(&st4[row * OP4 + cv * 8 + 4]);
+          float gv[8];
+          if (a.in_f32) {
+            const uint32_t go = (uint32_t)row * (uint32_t)a.sg_t * 4 + cv * 32;
+            const f32x4 g0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, go, 0, 0));
+            const f32x4 g1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, go + 16, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              gv[e] = g0[e];
+              gv[4 + e] = g1[e];
+            }
+          } else {
+            const uint32_t go = (uint32_t)row * (uint32_t)a.sg_t * 2 + cv * 16;
+            const bf16x8 gb = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsg, go, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[e] = bf16v_to_f32(gb[e]);
+          }
+          float out[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float yv = e < 4 ? y0[e] : y1[e - 4];
+            out[e] = yv * (gv[e] / (1.0f + expf(-gv[e])));
+          }
+          if (a.o_f32) {
+            const uint32_t oo = (uint32_t)row * (uint32_t)a.so_t * 4 + cv * 32;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{out[0], out[1], out[2], out[3]}), rso, oo, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{out[4], out[5], out[6], out[7]}), rso, oo + 16, 0, 0);
+          } else {
+            bf16x8 pk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[e] = (__bf16)out[e];
+            const uint32_t oo = (uint32_t)row * (uint32_t)a.so_t * 2 + cv * 16;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pk), rso, oo, 0, 0);
+          }
+        }
+      }
+    } else if constexpr (!SO) {
       const int f32o = a.o_f32;
       bf16_t* stg = STG_IN_P ? sP : sQP;
       if (f32o) {
@@ -773,10 +946,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   }
 }
 
-template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO>
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false>
 __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT>::BYTES];
-  chunk_body<DK, DV, BN, NW, C, NT, REV, SO>(a, blockIdx.x, smem);
+  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW, EPI>::BYTES];
+  chunk_body<DK, DV, BN, NW, C, NT, REV, SO, EPI>(a, blockIdx.x, smem);
 }
 
 // Two independent passes of one shape in one launch, the first in forward
@@ -784,7 +957,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
 // run a1.  Each pass alone fills half the GPU.
 template <int DK, int DV, int BN, int NW, int C, int NT, bool SO>
 __global__ void __launch_bounds__(NW * 64) chunk_kernel_pair(ChunkArgs a0, ChunkArgs a1, int nb0) {
-  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT>::BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW>::BYTES];
   const int xb = blockIdx.x;
   if (xb < nb0) chunk_body<DK, DV, BN, NW, C, NT, false, SO>(a0, xb, smem);
   else chunk_body<DK, DV, BN, NW, C, NT, true, SO>(a1, xb - nb0, smem);
@@ -826,6 +999,61 @@ static hipError_t launch_pair(const ChunkArgs& a0, const ChunkArgs& a1, hipStrea
   return hipGetLastError();
 }
 
+// Forward with the output epilogue: every column of a head in one workgroup
+// (the state pass of a segment split runs the same tiling without it).
+template <int DK, int DV, int BN, int NW, int C, int NT>
+static hipError_t launch_epi(const ChunkArgs& a, hipStream_t st) {
+  static_assert(DV == BN, "the epilogue needs whole heads");
+  const int64_t BH = a.B * a.H;
+  const int64_t nblocks = (BH + 7) / 8 * 8 * a.nseg;
+  if (nblocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)nblocks), block(NW * 64);
+  if (a.nseg > 1) {
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false, true, false>), grid, block, 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false, false, true>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+bool chunk_fused_supported(int dk, int dv, int chunk, int in_f32) {
+  const bool big = dk == 96 && dv == 192, small = dk == 16 && dv == 32;
+  if (!(big || small)) return false;
+  if (big) return in_f32 ? (chunk == 16 || chunk == 32) : (chunk == 16 || chunk == 32 || chunk == 64);
+  return chunk == 16 || chunk == 32 || chunk == 64;
+}
+
+int chunk_segments_fused(int64_t B, int64_t H, int64_t T, int chunk) {
+  return segments_for_units(B * H, T, chunk);
+}
+
+hipError_t launch_chunk_fused(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st) {
+  if (!chunk_fused_supported(dk, dv, chunk, a.in_f32) || a.reverse) return hipErrorInvalidValue;
+  if (dk == 96) {
+    if (!a.in_f32) {
+      switch (chunk) {
+        case 16: return launch_epi<96, 192, 192, 12, 16, 1>(a, st);
+        case 32: return launch_epi<96, 192, 192, 12, 32, 1>(a, st);
+        default: return launch_epi<96, 192, 192, 12, 64, 1>(a, st);
+      }
+    }
+    return chunk == 16 ? launch_epi<96, 192, 192, 12, 16, 3>(a, st) : launch_epi<96, 192, 192, 12, 32, 3>(a, st);
+  }
+  if (!a.in_f32) {
+    switch (chunk) {
+      case 16: return launch_epi<16, 32, 32, 2, 16, 1>(a, st);
+      case 32: return launch_epi<16, 32, 32, 2, 32, 1>(a, st);
+      default: return launch_epi<16, 32, 32, 2, 64, 1>(a, st);
+    }
+  }
+  switch (chunk) {
+    case 16: return launch_epi<16, 32, 32, 2, 16, 3>(a, st);
+    case 32: return launch_epi<16, 32, 32, 2, 32, 3>(a, st);
+    default: return launch_epi<16, 32, 32, 2, 64, 3>(a, st);
+  }
+}
+
 // column-block width per shape and chunk (must match launch_shape)
 static int block_cols(int dk, int dv, int chunk) {
   if (dk == 96 && dv == 192) return 96;
@@ -833,12 +1061,8 @@ static int block_cols(int dk, int dv, int chunk) {
   return dv;  // the small shapes run all columns in one workgroup
 }
 
-int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk) {
+int segments_for_units(int64_t units, int64_t T, int chunk) {
   constexpr int64_t kTargetUnits = 256;  // one workgroup per compute unit of an MI355X
-  const int nblk = dv / block_cols(dk, dv, chunk);
-  // the backward's two transposed passes share one launch when each has a
-  // single column block (launch_tiles)
-  const int64_t units = B * H * nblk * ((dk > dv && nblk == 1) ? 2 : 1);
   const int64_t nchunks = (T + chunk - 1) / chunk;
   if (units >= kTargetUnits || nchunks < 4) return 1;
   int64_t nseg = (kTargetUnits + units - 1) / units;
@@ -848,6 +1072,13 @@ int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk) {
   // equal segments of whole chunks; drop any that would be empty
   const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
   return (int)((nchunks + seg_chunks - 1) / seg_chunks);
+}
+
+int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk) {
+  const int nblk = dv / block_cols(dk, dv, chunk);
+  // the backward's two transposed passes share one launch when each has a
+  // single column block (launch_tiles)
+  return segments_for_units(B * H * nblk * ((dk > dv && nblk == 1) ? 2 : 1), T, chunk);
 }
 
 // One pass, or (a1 != null) two passes of the backward's transposed shape in

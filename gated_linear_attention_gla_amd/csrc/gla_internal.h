@@ -49,6 +49,15 @@ struct ChunkArgs {
   int64_t pool_stride_n, num_slots;
   const int32_t* slots;
   const int32_t* has_state;
+  // Output epilogue (forward with every column of a head in one workgroup):
+  // o' = o + sigmoid(q . (aug_h * k)) v, y = o' / sqrt(mean(o'^2) + eps) *
+  // gamma_h * SiLU(gz), written to o.  gz: the gate stream, (b, h, t, d)
+  // strides like the other inputs and in their dtype.
+  const void* gz;
+  int64_t sg_b, sg_h, sg_t;
+  const float* aug;    // [H][DK]
+  const float* gamma;  // [H][DV]
+  float eps;
 };
 
 struct DecodeArgs {
@@ -107,6 +116,12 @@ hipError_t launch_chunk_pair(int dk, int dv, int chunk, const ChunkArgs& a0, con
 // they need: enough (b, h, column block, segment) units to fill the GPU.
 int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk);
 bool chunk_pass_supported(int dk, int dv, int chunk, int in_f32);
+// Segments for a given number of (b, h, column block) units.
+int segments_for_units(int64_t units, int64_t T, int chunk);
+// Forward with the fused output epilogue (whole heads per workgroup).
+bool chunk_fused_supported(int dk, int dv, int chunk, int in_f32);
+int chunk_segments_fused(int64_t B, int64_t H, int64_t T, int chunk);
+hipError_t launch_chunk_fused(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st);
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
 bool decode_supported(int dk, int dv);
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);

@@ -227,3 +227,18 @@ def random_chunk_inputs(seed, B, H, T, dk, dv, dtype="f32", s0=True, dS_T=False,
         dS_T=normal(seed, TID["dS_T"], (B, H, dk, dv), 0.5, "f32") if dS_T else None,
     )
     return out
+
+
+EPI_TID = {"g": 11, "aug": 12, "gamma": 13}
+
+
+def epilogue_inputs(seed, B, H, T, dk, dv, dtype="bf16", aug_scale=0.5):
+    """Gate stream g ~ N(0, 1) (storage dtype, (B, H, T, dv)), per-channel
+    balance aug ~ N(0, aug_scale^2) (aug_scale 0: the initial a = 0) and
+    RMSNorm weights gamma ~ 1 + N(0, 0.1^2), fp32."""
+    return dict(
+        g=normal(seed, EPI_TID["g"], (B, H, T, dv), 1.0, dtype),
+        aug=(normal(seed, EPI_TID["aug"], (H, dk), aug_scale, "f32") if aug_scale
+             else np.zeros((H, dk))),
+        gamma=round_f32(1.0 + rng(seed, EPI_TID["gamma"]).standard_normal((H, dv)) * 0.1),
+    )

@@ -151,6 +151,30 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
                            const gla_tensor* k, const gla_tensor* v, const float* lambda,
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream);
 
+/* Chunked forward with the mixer's output epilogue fused into the store
+ * (page section "GLA mixer", after the readout: self-augmentation adds a
+ * gated copy of the value, the gate being the sigmoid of the query-key dot
+ * product with a learned per-channel scale a, zero at initialisation; each
+ * head's output then goes through the Head RMSNorm of its decay tier and is
+ * gated by SiLU(g_t) before the output projection).  Per token and head:
+ *   o' = o + sigmoid(sum_i q[i] aug[h][i] k[i]) v
+ *   y  = o' / sqrt(mean_j o'[j]^2 + eps) * gamma[h] * SiLU(g)
+ * with o the output of gla_chunk_fwd; y replaces o.
+ *   g      the gate stream [B,H,T,dv] (same dtype and view rules as q, k, v;
+ *          the model's token-major [B, T, H*dv] layout is the view with
+ *          stride_h = dv, stride_t = H*dv)
+ *   aug    fp32 [H][dk];  gamma fp32 [H][dv] (a tier's RMSNorm weight,
+ *          repeated for each head of the tier);  eps >= 0 (GLA_ERR_SHAPE
+ *          otherwise)
+ * Shapes: (dk, dv) in {(96, 192), (16, 32)}; chunk in {16, 32, 64} (fp32
+ * inputs at (96, 192): 16 or 32).  Workspace from
+ * gla_chunk_fwd_fused_workspace (segment states, as for gla_chunk_fwd). */
+size_t gla_chunk_fwd_fused_workspace(const gla_dims* dims);
+gla_status gla_chunk_fwd_fused(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                               const gla_tensor* v, const float* lambda, const float* S0,
+                               const gla_tensor* g, const float* aug, const float* gamma, float eps,
+                               gla_tensor* y, float* S_T, void* ws, size_t ws_bytes, void* stream);
+
 /* Variable-length batched prefill straight into the decode state pool (page
  * sections "GLA mixer" and "Inference optimization on Trainium2": each
  * sequence owns one fixed-size state page that prefill fills and every decode

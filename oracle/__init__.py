@@ -19,7 +19,7 @@ import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "gla_oracle.c")
-_SRCS = [_SRC, os.path.join(_DIR, "gla_conv_oracle.c")]
+_SRCS = [_SRC, os.path.join(_DIR, "gla_conv_oracle.c"), os.path.join(_DIR, "gla_epilogue_oracle.c")]
 _LIB_PATH = os.path.join(_DIR, "liboracle.so")
 _LIB = None
 
@@ -50,6 +50,7 @@ def _lib():
         lib.gla_oracle_decode_step.argtypes = [i64] * 4 + [dp] * 6
         lib.gla_oracle_num_threads.restype = ctypes.c_int
         lib.gla_oracle_conv1d.argtypes = [i64] * 4 + [dp] * 6
+        lib.gla_oracle_epilogue.argtypes = [i64] * 5 + [dp] * 6 + [ctypes.c_double] + [dp] * 2
         lib.gla_oracle_conv1d_step.argtypes = [i64] * 3 + [dp] * 5
         _LIB = lib
     return _LIB
@@ -176,3 +177,16 @@ def conv1d_step(x, w, bias, state):
     y = np.zeros((N, D))
     _lib().gla_oracle_conv1d_step(N, D, W, _p(x), _p(w), _p(bias), _p(st), _p(y))
     return y, st
+
+
+def epilogue(q, k, v, o, a, gamma, eps, g):
+    """Mixer output epilogue (self-augmentation, Head RMSNorm, SiLU gate):
+    q, k (B, H, T, dk); v, o, g (B, H, T, dv); a (H, dk); gamma (H, dv).
+    Returns y (B, H, T, dv); see gla_epilogue_oracle.c."""
+    q, k, v, o, a, gamma, g = map(_f64, (q, k, v, o, a, gamma, g))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    y = np.zeros((B, H, T, dv))
+    _lib().gla_oracle_epilogue(B, H, T, dk, dv, _p(q), _p(k), _p(v), _p(o), _p(a), _p(gamma),
+                               float(eps), _p(g), _p(y))
+    return y
