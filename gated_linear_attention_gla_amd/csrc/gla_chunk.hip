@@ -777,6 +777,33 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
     }
     if constexpr (EPI && !SO) {
+      // this chunk's gate-stream values for the store below, loaded now so
+      // their latency overlaps the normalisation (8 columns per thread)
+      const int ges = a.in_f32 ? 4 : 2;
+      const char* gbase =
+          reinterpret_cast<const char*>(a.gz) + (b * a.sg_b + h * a.sg_h + (tbase + t0) * a.sg_t) * ges;
+      const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(gbase), (short)0, (int)(((uint32_t)(L - 1) * (uint32_t)a.sg_t + BN) * ges), 0x00020000);
+      constexpr int VPR8 = BN / 8;
+      static_assert(NTHR % VPR8 == 0, "threads must cover whole rows");
+      constexpr int RPJ8 = NTHR / VPR8;
+      constexpr int NJ8 = (CP + RPJ8 - 1) / RPJ8;
+      const int row0 = tid / VPR8;
+      const int cv = tid - row0 * VPR8;
+      u32x4 graw[NJ8][NT == 3 ? 2 : 1];
+#pragma unroll
+      for (int j = 0; j < NJ8; ++j) {
+        const int row = row0 + j * RPJ8;
+        if (CP % RPJ8 == 0 || row < CP) {
+          if constexpr (NT == 3) {
+            const uint32_t go = (uint32_t)row * (uint32_t)a.sg_t * 4 + cv * 32;
+            graw[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rsg, go, 0, 0);
+            graw[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rsg, go + 16, 0, 0);
+          } else {
+            graw[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rsg, (uint32_t)row * (uint32_t)a.sg_t * 2 + cv * 16, 0, 0);
+          }
+        }
+      }
       // o' = o + gate v, then per-row sums of squares over this wave's columns
 #pragma unroll
       for (int I = 0; I < CT; ++I) {
@@ -818,38 +845,26 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       __syncthreads();
       // y * SiLU(gate stream): 8 columns per thread, coalesced 16-byte rows
       const int oes = a.o_f32 ? 4 : 2;
-      const int ges = a.in_f32 ? 4 : 2;
       char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + (tbase + t0) * a.so_t) * oes;
-      const char* gbase =
-          reinterpret_cast<const char*>(a.gz) + (b * a.sg_b + h * a.sg_h + (tbase + t0) * a.sg_t) * ges;
       const __amdgpu_buffer_rsrc_t rso = __builtin_amdgcn_make_buffer_rsrc(
           obase, (short)0, (int)(((uint32_t)(L - 1) * (uint32_t)a.so_t + BN) * oes), 0x00020000);
-      const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char*>(gbase), (short)0, (int)(((uint32_t)(L - 1) * (uint32_t)a.sg_t + BN) * ges), 0x00020000);
-      constexpr int VPR8 = BN / 8;
-      static_assert(NTHR % VPR8 == 0, "threads must cover whole rows");
-      constexpr int RPJ8 = NTHR / VPR8;
-      const int row0 = tid / VPR8;
-      const int cv = tid - row0 * VPR8;
 #pragma unroll
-      for (int j = 0; j < (CP + RPJ8 - 1) / RPJ8; ++j) {
+      for (int j = 0; j < NJ8; ++j) {
         const int row = row0 + j * RPJ8;
         if (CP % RPJ8 == 0 || row < CP) {
           const f32x4 y0 = *reinterpret_cast<const f32x4*>(&st4[row * OP4 + cv * 8]);
           const f32x4 y1 = *reinterpret_cast<const f32x4*>(&st4[row * OP4 + cv * 8 + 4]);
           float gv[8];
-          if (a.in_f32) {
-            const uint32_t go = (uint32_t)row * (uint32_t)a.sg_t * 4 + cv * 32;
-            const f32x4 g0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, go, 0, 0));
-            const f32x4 g1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, go + 16, 0, 0));
+          if constexpr (NT == 3) {
+            const f32x4 g0 = __builtin_bit_cast(f32x4, graw[j][0]);
+            const f32x4 g1 = __builtin_bit_cast(f32x4, graw[j][NT == 3 ? 1 : 0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               gv[e] = g0[e];
               gv[4 + e] = g1[e];
             }
           } else {
-            const uint32_t go = (uint32_t)row * (uint32_t)a.sg_t * 2 + cv * 16;
-            const bf16x8 gb = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsg, go, 0, 0));
+            const bf16x8 gb = __builtin_bit_cast(bf16x8, graw[j][0]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) gv[e] = bf16v_to_f32(gb[e]);
           }
