@@ -154,6 +154,16 @@ constexpr int pitch_p(int cp) {
   }
 }
 
+// Key-tile row pitch: the smallest >= DKP (multiple of 8 elements) whose byte
+// pitch mod 256 is 192 -- the transposing column reads of the state update
+// (16 lanes: 4 rows x 4 column groups 16 bytes apart) then cost the minimum
+// 4 LDS cycles; the 16-byte row reads of the P tiles pay 4 extra cycles, but
+// they are 5 times fewer.
+constexpr int pitch_kt(int dkp) {
+  for (int p = dkp;; p += 8)
+    if ((2 * p) % 256 == 192) return p;
+}
+
 // State row held in accumulator slot r of row tile D by lane group g.  With DK
 // a multiple of 32 the two tiles of each 32-row block interleave in runs of 4
 // (tile 2m + h, group g: rows 32 m + 8 g + 4 h + r), so the 8 k-slots a lane
@@ -174,11 +184,13 @@ struct ChunkLds {
   static constexpr int DKP = (DK + 31) / 32 * 32;  // DK padded likewise
   static constexpr int NTP = NT == 3 ? 3 : 2;      // terms of the masked P tile
   // LDS row pitches (elements), chosen from measured bank-conflict rates of
-  // each tile's access mix on gfx950: the query tile is read with 16-byte row
-  // reads, the key tile with 16-byte row reads and column reads, the P tile
-  // with 16-byte row reads, the value tile with column reads.
-  static constexpr int PQ = DKP + 8;
-  static constexpr int PK = DKP + 16;
+  // each tile's access mix on gfx950 (rocprofv3 SQ_LDS_BANK_CONFLICT per
+  // pattern): the query and P tiles are read with 16-byte row reads
+  // (conflict-free when the byte pitch mod 256 is 32, 160 or 224), the key
+  // tile mostly with column reads (pitch_kt), the value tile with column reads
+  // (the same cost at any pitch).
+  static constexpr int PQ = DKP >= 32 ? pitch_p(DKP - 8) : DKP + 8;
+  static constexpr int PK = pitch_kt(DKP);
   static constexpr int PVV = BN + 16;
   static constexpr int PP = pitch_p(CP);
   static constexpr int Q_ELEMS = NT * CP * PQ;
@@ -194,9 +206,16 @@ struct ChunkLds {
   static constexpr int OP2 = BN + 8;
   static constexpr int OP4 = BN + 4;
   static constexpr int STG_ELEMS = CP * OP4 * 2;  // bf16 units, fp32 case (the larger)
-  static constexpr int QP_RAW = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS) : Q_ELEMS + P_ELEMS;
+  // The P region also holds the staged output when there is room for both
+  // (then the next query tile can land before the output is staged, which
+  // saves a barrier per chunk).
+  static constexpr int P_REGION = P_ELEMS > STG_ELEMS ? P_ELEMS : STG_ELEMS;
+  static constexpr bool STG_IN_P =
+      !ALIAS_P && (STG_ELEMS <= P_ELEMS ||
+                   2 * (Q_ELEMS + K_ELEMS + V_ELEMS + P_REGION) + 4 * (3 * CP + 2) <= 160 * 1024 - 8192);
+  static constexpr int QP_RAW = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS)
+                                        : Q_ELEMS + (STG_IN_P ? P_REGION : P_ELEMS);
   static constexpr int QP_ELEMS = QP_RAW > STG_ELEMS ? QP_RAW : STG_ELEMS;
-  static constexpr bool STG_IN_P = !ALIAS_P && STG_ELEMS <= P_ELEMS;
   // byte offsets (every region 16-byte aligned)
   static constexpr int OFF_K = 2 * QP_ELEMS;
   static constexpr int OFF_V = OFF_K + 2 * K_ELEMS;
