@@ -217,12 +217,23 @@ def bench_decode(gla, inputs, steps_override=None):
     calls = steps * Lyr
     nbytes = calls * N * H * DEC_BYTES
     per_call_ms = ms / calls
+    # the same layer call with the output epilogue fused (gate stream g bf16)
+    gz = torch.randn((N, H, DV), generator=g, device="cuda").to(torch.bfloat16)
+    aug = torch.zeros((H, DK), dtype=torch.float32, device="cuda")
+    gam = torch.ones((H, DV), dtype=torch.float32, device="cuda")
+    blk = qkv[0, 0]
+    fused = lambda: gla.decode_step_fused_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, S[0], gz,
+                                           aug, gam, 1e-6, y=o)
+    fused()
+    torch.cuda.synchronize()
+    fused_ms = event_time_ms(fused, 20, stream)
     return dict(
         workload="decode: 1280 seqs x 24 layers x H=16, fp32 96x192 states, 64 steps, bf16 q/k/v",
         N=N, layers=Lyr, H=H, steps=steps, ms_total=ms, ms_per_layer_call=per_call_ms,
         tokens_per_s=N * steps / (ms / 1e3), gbs=nbytes / (ms / 1e3) / 1e9,
         hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         state_gb=S.numel() * 4 / 1e9,
+        ms_per_layer_call_fused_epilogue=fused_ms,
     )
 
 

@@ -97,6 +97,12 @@ def load_library(path=LIB_PATH):
         P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
         P(GlaTensor), vp,
     ]
+    lib.gla_decode_step_fused.restype = ctypes.c_int
+    lib.gla_decode_step_fused.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
+        P(GlaTensor), vp, vp, ctypes.c_float, P(GlaTensor), vp,
+    ]
     lib.gla_chunk_fwd_fused_workspace.restype = ctypes.c_size_t
     lib.gla_chunk_fwd_fused_workspace.argtypes = [P(GlaDims)]
     lib.gla_chunk_fwd_fused.restype = ctypes.c_int
@@ -284,6 +290,30 @@ def chunk_fwd_fused(q, k, v, lam, g, aug, gamma, eps=1e-6, S0=None, chunk=64, ou
     )
     _check(lib, st)
     return y, S_T
+
+
+def decode_step_fused_(q, k, v, lam, S, g, aug, gamma, eps=1e-6, y=None, out_dtype=None):
+    """y = decode_step_fused_(q, k, v, lam, S, g, aug, gamma, eps): one
+    recurrent step (S in place) with the output epilogue; g (N, H, dv)."""
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError("S must be float32 of shape (N, H, dk, dv)")
+    if S.stride()[1:] != (dk * dv, dv, 1):
+        raise ValueError("each sequence's heads must be dense in S")
+    for name, t, shp in (("aug", aug, (H, dk)), ("gamma", gamma, (H, dv))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shp}")
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype or q.dtype, device=q.device)
+    tq, tk, tv, tg, ty = _view3(q), _view3(k), _view3(v), _view3(g), _view3(y)
+    st = lib.gla_decode_step_fused(
+        N, H, dk, dv, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(lam), _ptr(S), S.stride(0),
+        ctypes.byref(tg), _ptr(aug), _ptr(gamma), ctypes.c_float(eps), ctypes.byref(ty), _stream(),
+    )
+    _check(lib, st)
+    return y
 
 
 def _packed(x):

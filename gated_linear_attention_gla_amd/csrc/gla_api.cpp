@@ -226,9 +226,10 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
   return GLA_OK;
 }
 
-gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
-                           const gla_tensor* k, const gla_tensor* v, const float* lambda,
-                           float* S, int64_t S_stride_n, gla_tensor* o, void* stream) {
+static gla_status decode_impl(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
+                              const gla_tensor* k, const gla_tensor* v, const float* lambda, float* S,
+                              int64_t S_stride_n, const gla_tensor* g, const float* aug, const float* gamma,
+                              float eps, gla_tensor* o, void* stream) {
   if (!q || !k || !v || !lambda || !S || !o) return GLA_ERR_NULL;
   if (N < 1 || H < 1 || dk < 1 || dv < 1 || N > (int64_t)1 << 30 || H > (int64_t)1 << 16 ||
       N * H > (int64_t)1 << 31)
@@ -243,6 +244,16 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
   if ((st = check_view(k, N, H, 1, dk, 1, true)) != GLA_OK) return st;
   if ((st = check_view(v, N, H, 1, dv, 1, true)) != GLA_OK) return st;
   if ((st = check_view(o, N, H, 1, dv, 1, true)) != GLA_OK) return st;
+  if (g) {
+    if (!aug || !gamma) return GLA_ERR_NULL;
+    if (g->dtype != q->dtype) return GLA_ERR_DTYPE;
+    if (!(eps >= 0.0f) || eps > 1e30f) return GLA_ERR_SHAPE;
+    if ((st = check_view(g, N, H, 1, dv, 1, true)) != GLA_OK) return st;
+    if (!aligned16(aug) || !aligned16(gamma)) return GLA_ERR_STRIDE;
+    if (same(o->data, g->data) || same(o->data, aug) || same(o->data, gamma) || same(S, g->data) ||
+        same(S, aug) || same(S, gamma))
+      return GLA_ERR_ALIAS;
+  }
   if (!aligned16(S) || !aligned16(lambda) || (N > 1 && (S_stride_n * 4) % 16 != 0)) return GLA_ERR_STRIDE;
   const void* ins[] = {q->data, k->data, v->data, lambda};
   for (const void* p : ins)
@@ -262,9 +273,31 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
   a.N = N; a.H = H;
   a.o_f32 = o->dtype == GLA_F32;
   a.in_f32 = q->dtype == GLA_F32;
+  if (g) {
+    a.gz = g->data;
+    a.sg_n = g->stride_b;
+    a.sg_h = g->stride_h;
+    a.aug = aug;
+    a.gamma = gamma;
+    a.eps = eps;
+  }
   if (gla::launch_decode((int)dk, (int)dv, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
+}
+
+gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
+                           const gla_tensor* k, const gla_tensor* v, const float* lambda,
+                           float* S, int64_t S_stride_n, gla_tensor* o, void* stream) {
+  return decode_impl(N, H, dk, dv, q, k, v, lambda, S, S_stride_n, nullptr, nullptr, nullptr, 0.0f, o, stream);
+}
+
+gla_status gla_decode_step_fused(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
+                                 const gla_tensor* k, const gla_tensor* v, const float* lambda, float* S,
+                                 int64_t S_stride_n, const gla_tensor* g, const float* aug,
+                                 const float* gamma, float eps, gla_tensor* y, void* stream) {
+  if (!g) return GLA_ERR_NULL;
+  return decode_impl(N, H, dk, dv, q, k, v, lambda, S, S_stride_n, g, aug, gamma, eps, y, stream);
 }
 
 size_t gla_chunk_fwd_fused_workspace(const gla_dims* dims) {

@@ -17,7 +17,7 @@
 
 namespace gla {
 
-template <int DK, int DV, int RP>
+template <int DK, int DV, int RP, bool EPI = false>
 __global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
   constexpr int CG = DV / 4;          // float4 column groups
   constexpr int NTHR = CG * RP;
@@ -84,24 +84,72 @@ __global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
       acc.w = fmaf(qd, s[3], acc.w);
     }
   }
+  // epilogue gate sigmoid(q . (aug * k)), reduced by the first wave
+  __shared__ float sgate;
+  if constexpr (EPI) {
+    if (tid < 64) {
+      float part = 0.0f;
+      for (int d = tid; d < DK; d += 64) part = fmaf(sq[d] * a.aug[h * DK + d], sk[d], part);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+      if (tid == 0) sgate = 1.0f / (1.0f + expf(-part));
+    }
+  }
   so[rp][cg] = acc;
   __syncthreads();
-  if (tid < CG) {
-    float4 r = so[0][tid];
+  static_assert(CG <= 64, "the first wave finishes the output");
+  if (tid < 64) {
+    const bool own = tid < CG;  // lanes that own a column group
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (own) {
+      r = so[0][tid];
 #pragma unroll
-    for (int p = 1; p < RP; ++p) {
-      const float4 u = so[p][tid];
-      r.x += u.x; r.y += u.y; r.z += u.z; r.w += u.w;
+      for (int p = 1; p < RP; ++p) {
+        const float4 u = so[p][tid];
+        r.x += u.x; r.y += u.y; r.z += u.z; r.w += u.w;
+      }
     }
-    const int64_t oo = n * a.so_n + h * a.so_h + 4 * tid;
-    if (a.o_f32) {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + oo) = r;
-    } else {
-      bf16_t* p = reinterpret_cast<bf16_t*>(a.o) + oo;
-      p[0] = f32_to_bf16(r.x);
-      p[1] = f32_to_bf16(r.y);
-      p[2] = f32_to_bf16(r.z);
-      p[3] = f32_to_bf16(r.w);
+    if constexpr (EPI) {
+      // o' = o + gate v; Head RMSNorm over the DV columns held by this wave
+      // (lanes without columns add zero); times gamma and SiLU(g)
+      const float gt = sgate;
+      if (own) {
+        r.x = fmaf(gt, vv.x, r.x);
+        r.y = fmaf(gt, vv.y, r.y);
+        r.z = fmaf(gt, vv.z, r.z);
+        r.w = fmaf(gt, vv.w, r.w);
+      }
+      float ss = r.x * r.x + r.y * r.y + r.z * r.z + r.w * r.w;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + a.eps);
+      if (own) {
+        const float4 gm = *reinterpret_cast<const float4*>(a.gamma + h * DV + 4 * tid);
+        const int64_t og = n * a.sg_n + h * a.sg_h + 4 * tid;
+        float4 gv;
+        if (a.in_f32) {
+          gv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.gz) + og);
+        } else {
+          const bf16_t* p = reinterpret_cast<const bf16_t*>(a.gz) + og;
+          gv = make_float4(bf16_to_f32(p[0]), bf16_to_f32(p[1]), bf16_to_f32(p[2]), bf16_to_f32(p[3]));
+        }
+        r.x = r.x * rstd * gm.x * (gv.x / (1.0f + expf(-gv.x)));
+        r.y = r.y * rstd * gm.y * (gv.y / (1.0f + expf(-gv.y)));
+        r.z = r.z * rstd * gm.z * (gv.z / (1.0f + expf(-gv.z)));
+        r.w = r.w * rstd * gm.w * (gv.w / (1.0f + expf(-gv.w)));
+      }
+    }
+    if (own) {
+      const int64_t oo = n * a.so_n + h * a.so_h + 4 * tid;
+      if (a.o_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + oo) = r;
+      } else {
+        bf16_t* p = reinterpret_cast<bf16_t*>(a.o) + oo;
+        p[0] = f32_to_bf16(r.x);
+        p[1] = f32_to_bf16(r.y);
+        p[2] = f32_to_bf16(r.z);
+        p[3] = f32_to_bf16(r.w);
+      }
     }
   }
   (void)NTHR;
@@ -114,10 +162,13 @@ bool decode_supported(int dk, int dv) {
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st) {
   const int64_t nblocks = a.N * a.H;
   if (nblocks <= 0) return hipSuccess;
+  const bool epi = a.gz != nullptr;
   if (dk == 96 && dv == 192) {
-    hipLaunchKernelGGL((decode_kernel<96, 192, 4>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
+    if (epi) hipLaunchKernelGGL((decode_kernel<96, 192, 4, true>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<96, 192, 4>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
   } else if (dk == 16 && dv == 32) {
-    hipLaunchKernelGGL((decode_kernel<16, 32, 8>), dim3((unsigned)nblocks), dim3(8 * 8), 0, st, a);
+    if (epi) hipLaunchKernelGGL((decode_kernel<16, 32, 8, true>), dim3((unsigned)nblocks), dim3(8 * 8), 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<16, 32, 8>), dim3((unsigned)nblocks), dim3(8 * 8), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -73,6 +73,13 @@ struct DecodeArgs {
   int64_t N, H;
   int o_f32;
   int in_f32;
+  // output epilogue (the fused decode step): gate stream g [N, H, dv] view,
+  // aug [H][DK], gamma [H][DV], eps; null gz = plain step
+  const void* gz;
+  int64_t sg_n, sg_h;
+  const float* aug;
+  const float* gamma;
+  float eps;
 };
 
 // Depthwise causal convolution (width 4) + SiLU over [B][T][D] activations.

@@ -175,6 +175,16 @@ gla_status gla_chunk_fwd_fused(const gla_dims* dims, const gla_tensor* q, const 
                                const gla_tensor* g, const float* aug, const float* gamma, float eps,
                                gla_tensor* y, float* S_T, void* ws, size_t ws_bytes, void* stream);
 
+/* gla_decode_step with the same output epilogue as gla_chunk_fwd_fused
+ * applied to o before it is written (y replaces o):
+ *   g      the gate stream [N, H, dv] view (stride_b steps n, stride_h h;
+ *          same dtype as q, k, v)
+ *   aug    fp32 [H][dk]; gamma fp32 [H][dv]; eps >= 0. */
+gla_status gla_decode_step_fused(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
+                                 const gla_tensor* k, const gla_tensor* v, const float* lambda, float* S,
+                                 int64_t S_stride_n, const gla_tensor* g, const float* aug,
+                                 const float* gamma, float eps, gla_tensor* y, void* stream);
+
 /* Variable-length batched prefill straight into the decode state pool (page
  * sections "GLA mixer" and "Inference optimization on Trainium2": each
  * sequence owns one fixed-size state page that prefill fills and every decode

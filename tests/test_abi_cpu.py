@@ -308,3 +308,32 @@ def test_varlen_rejects_bad_arguments(lib):
     assert call(o=0x100000) == ALIAS
     assert call(pool=0x400000) == ALIAS
     assert call(dtype=9) == DTYPE
+
+
+def test_fused_entry_points_reject_bad_arguments(lib):
+    ref = ctypes.byref
+    q, k, v, o = views()
+    g = T(0x500000, sb=2 * 64 * 192, sh=64 * 192, st=192)
+    d = dims()
+    call = lambda dd=d, gg=g, aug=0xA000, gam=0xB000, eps=1e-6, y=o: lib.gla_chunk_fwd_fused(
+        ref(dd), ref(q), ref(k), ref(v), 0x9000, None, ref(gg) if gg else None, aug, gam, ctypes.c_float(eps),
+        ref(y), None, None, 0, None)
+    assert call(gg=None) == NULL
+    assert call(aug=None) == NULL
+    assert call(eps=-1.0) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(dd=dims(chunk=128)) == UNSUP
+    assert call(aug=0xA004) == STRIDE
+    assert call(y=T(0x500000, sb=2 * 64 * 192, sh=64 * 192, st=192)) == ALIAS
+    # decode with the epilogue
+    dq = T(0x100000, sb=2 * 96, sh=96)
+    dk_ = T(0x200000, sb=2 * 96, sh=96)
+    dv_ = T(0x300000, sb=2 * 192, sh=192)
+    dout = T(0x400000, sb=2 * 192, sh=192)
+    dg = T(0x500000, sb=2 * 192, sh=192)
+    dec = lambda gg=dg, aug=0xA000, y=dout: lib.gla_decode_step_fused(
+        4, 2, 96, 192, ref(dq), ref(dk_), ref(dv_), 0x9000, 0xC00000, 2 * 96 * 192, ref(gg) if gg else None,
+        aug, 0xB000, ctypes.c_float(1e-6), ref(y), None)
+    assert dec(gg=None) == NULL
+    assert dec(aug=None) == NULL
+    assert dec(y=T(0x500000, sb=2 * 192, sh=192)) == ALIAS

@@ -97,3 +97,28 @@ def test_fused_training_shape_sampled(gla):
         ey, eS = oracle.rel_err(y[sl], ry), oracle.rel_err(S[sl], rS)
         flush(f"  b={b} err y={ey:.3e} S_T={eS:.3e}")
         assert ey <= TOL["bf16"] and eS <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dims", [(16, 32, "f32"), (96, 192, "bf16"), (96, 192, "f32")])
+def test_fused_decode_steps(gla, dims):
+    """The decode step with the epilogue against oracle.decode_step followed
+    by oracle.epilogue, over several steps (state updated in place)."""
+    dk, dv, dtype = dims
+    flush(f"test_fused_decode_steps dk={dk} dv={dv} {dtype}")
+    N, H, steps = 29, 3, 4
+    x = inputs.random_chunk_inputs(760 + dk, N, H, steps, dk, dv, dtype=dtype, scale=1.0)
+    e = inputs.epilogue_inputs(760 + dk, N, H, steps, dk, dv, dtype, aug_scale=0.2)
+    S_host = inputs.normal(760 + dk, inputs.TID["S"], (N, H, dk, dv), 0.01, "f32")
+    S, lam, Sref = dev_f32(S_host), dev_f32(x["lam"]), S_host.copy()
+    aug, gam = dev_f32(e["aug"]), dev_f32(e["gamma"])
+    for t in range(steps):
+        q, k, v, g = (dev(np.ascontiguousarray(arr[:, :, t]), dtype)
+                      for arr in (x["q"], x["k"], x["v"], e["g"]))
+        y = gla.decode_step_fused_(q, k, v, lam, S, g, aug, gam, EPS, out_dtype=torch.float32)
+        ro, Sref = oracle.decode_step(x["q"][:, :, t], x["k"][:, :, t], x["v"][:, :, t], x["lam"], Sref)
+        sl = lambda a: a[:, :, t:t + 1]
+        ry = oracle.epilogue(sl(x["q"]), sl(x["k"]), sl(x["v"]), ro[:, :, None], e["aug"], e["gamma"], EPS,
+                             sl(e["g"]))[:, :, 0]
+        torch.cuda.synchronize()
+        assert oracle.rel_err(host(y), ry) <= 1e-5
+    assert oracle.rel_err(host(S), Sref) <= 1e-5
