@@ -457,8 +457,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   TileStager<NT, CP, DK, DKP, PK, NTHR> pfk;
   TileStager<NT, CP, BN, BN, PVV, NTHR> pfv;
   // With wide query/key rows the three prefetched tiles do not fit in
-  // registers next to the state and the P tile; the next query tile is then
-  // fetched only after stage 4, while the output is staged and stored.
+  // registers next to the state, the P tile and the readout; the next query
+  // tile is then fetched only after stage 2 (the register peak).
   constexpr bool LATE_Q = DK > 128;
   auto prefetch_q = [&](int64_t ci) {
     const int64_t t0 = chunk_start(ci);
@@ -667,6 +667,11 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       }
     }
     if constexpr (!SO) __syncthreads();  // P complete
+    // wide query rows: the next query tile is fetched now, once the readout's
+    // registers are free, and written to LDS at the end of the chunk
+    if constexpr (LATE_Q && !SO) {
+      if (ci + 1 < nchunks) prefetch_q(ci + 1);
+    }
     if constexpr (EPI && !SO) {
       for (int row = tid; row < CP; row += NTHR) {
         float sdot = 0.0f;
@@ -790,7 +795,6 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       pfk.store(sK, tid);
       pfv.store(sV, tid);
       if constexpr (STG_IN_P && !LATE_Q && !SO) pfq.store(sQ, tid);
-      if constexpr (LATE_Q && !SO) prefetch_q(ci + 1);  // lands after the output is out
     }
     if constexpr (STG_IN_P) {
       if (refill) fill_factors(chunk_len(chunk_start(ci + 1)));
