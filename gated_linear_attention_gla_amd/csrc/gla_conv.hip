@@ -23,7 +23,7 @@ namespace {
 
 constexpr int CW = 4;        // convolution width
 constexpr int CT = 16;       // tokens per thread run
-constexpr int CTHR = 128;    // threads per workgroup (1,024 channels)
+constexpr int CTHR = 64;     // threads per workgroup (512 channels)
 
 // 8 stored input values held between the load and their use (raw, so a bf16
 // row costs 4 registers while its load is in flight)
@@ -83,7 +83,8 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const float (&v)
 // z -> -inf the reciprocal of +inf is 0, so the result tends to -0.
 __device__ __forceinline__ float silu(float z) { return z * __frcp_rn(1.0f + __expf(-z)); }
 
-// taps of 8 channels: wt[j][e] = w[c0 + e][j]
+// taps of 8 channels: wt[j][e] = w[c0 + e][j]; the bias as two 16-byte
+// vectors (a lane's 8 biases are contiguous)
 __device__ __forceinline__ void load_taps(const float* w, const float* bias, int64_t c0, float (&wt)[CW][8],
                                           float (&bs)[8]) {
 #pragma unroll
@@ -91,7 +92,16 @@ __device__ __forceinline__ void load_taps(const float* w, const float* bias, int
     const f32x4 t = *reinterpret_cast<const f32x4*>(w + (c0 + e) * CW);
 #pragma unroll
     for (int j = 0; j < CW; ++j) wt[j][e] = t[j];
-    bs[e] = bias ? bias[c0 + e] : 0.0f;
+  }
+  f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+  if (bias) {
+    b0 = *reinterpret_cast<const f32x4*>(bias + c0);
+    b1 = *reinterpret_cast<const f32x4*>(bias + c0 + 4);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bs[e] = b0[e];
+    bs[4 + e] = b1[e];
   }
 }
 
@@ -112,7 +122,6 @@ __global__ void __launch_bounds__(CTHR) conv_fwd_kernel(ConvArgs a) {
   const int64_t t0 = run * CT;
   const int64_t t1 = (a.T - t0) < CT ? a.T : t0 + CT;
   float wt[CW][8], bs[8];
-  load_taps(a.w, a.bias, c0, wt, bs);
 
   // window: the 3 inputs before t0 (from x, else from the carried window)
   float h[CW - 1][8];
@@ -147,7 +156,9 @@ __global__ void __launch_bounds__(CTHR) conv_fwd_kernel(ConvArgs a) {
       if (t < t1) load_raw<IN_F32>(a.x, b * a.sx_b + t * a.sx_t + c0, dst[u]);
     }
   };
+  // the first rows go out before the taps: they come from HBM, the taps from L2
   load_group(0, xr[0]);
+  load_taps(a.w, a.bias, c0, wt, bs);
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     if (gi + 1 < G) load_group(gi + 1, xr[(gi + 1) & 1]);
