@@ -251,14 +251,18 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     return dict(bytes=nbytes, reps=reps)
 
 
+# the sources that decide the chunked backward's kernels and launches
+CHUNK_SOURCES = ("gla_api.cpp", "gla_chunk.hip", "gla_common.hpp", "gla_internal.h")
+
+
 def kernel_source_digest():
-    """sha256 over the HIP sources; traffic figures are only valid for the
-    sources they were counted on."""
+    """sha256 over the chunked kernels' sources; traffic figures are only
+    valid for the sources they were counted on."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(REPO, "gated_linear_attention_gla_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in CHUNK_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
