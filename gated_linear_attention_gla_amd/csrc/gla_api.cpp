@@ -56,10 +56,16 @@ gla_status check_view(const gla_tensor* x, int64_t nb, int64_t nh, int64_t nt, i
 
 bool same(const void* a, const void* b) { return a != nullptr && a == b; }
 
+// A launch covers at most 2^32 - 1 work-items (the dispatch packet's grid
+// size is 32 bits): with up to 768 threads per workgroup and two column blocks
+// (four workgroups per (b, h) in the backward's paired launch), B * H <= 2^21
+// keeps every chunked launch below it.
+constexpr int64_t kMaxUnits = (int64_t)1 << 21;
+
 gla_status check_dims(const gla_dims* d) {
   if (d->B < 1 || d->H < 1 || d->T < 0 || d->dk < 1 || d->dv < 1 || d->chunk < 1) return GLA_ERR_SHAPE;
   if (d->B > (int64_t)1 << 24 || d->H > (int64_t)1 << 16 || d->T > (int64_t)1 << 40) return GLA_ERR_SHAPE;
-  if (d->B * d->H > (int64_t)1 << 26) return GLA_ERR_SHAPE;
+  if (d->B * d->H > kMaxUnits) return GLA_ERR_SHAPE;
   return GLA_OK;
 }
 
@@ -231,8 +237,10 @@ static gla_status decode_impl(int64_t N, int64_t H, int64_t dk, int64_t dv, cons
                               int64_t S_stride_n, const gla_tensor* g, const float* aug, const float* gamma,
                               float eps, gla_tensor* o, void* stream) {
   if (!q || !k || !v || !lambda || !S || !o) return GLA_ERR_NULL;
+  // one workgroup of dv / 4 * 4 threads per (n, h): N * H <= 2^24 keeps the
+  // launch below 2^32 work-items
   if (N < 1 || H < 1 || dk < 1 || dv < 1 || N > (int64_t)1 << 30 || H > (int64_t)1 << 16 ||
-      N * H > (int64_t)1 << 31)
+      N * H > (int64_t)1 << 24)
     return GLA_ERR_SHAPE;
   if (!dtype_ok(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype || !dtype_ok(o->dtype))
     return GLA_ERR_DTYPE;
@@ -360,7 +368,7 @@ gla_status gla_chunk_fwd_varlen(int64_t N, int64_t H, int64_t total_T, int64_t d
                                 void* stream) {
   if (!q || !k || !v || !o || !cu_seqlens || !lambda || !pool) return GLA_ERR_NULL;
   if (N < 1 || H < 1 || total_T < 0 || num_slots < 1 || N > ((int64_t)1 << 24) || H > ((int64_t)1 << 16) ||
-      N * H > ((int64_t)1 << 26) || total_T > ((int64_t)1 << 31) - 1 || num_slots > ((int64_t)1 << 31))
+      N * H > kMaxUnits || total_T > ((int64_t)1 << 31) - 1 || num_slots > ((int64_t)1 << 31))
     return GLA_ERR_SHAPE;
   if (!dtype_ok(q->dtype) || !dtype_ok(o->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
     return GLA_ERR_DTYPE;
@@ -421,7 +429,7 @@ gla_status gla_conv1d_fwd(int64_t B, int64_t T, int64_t D, const gla_tensor* x, 
   if (!x || !w || !y) return GLA_ERR_NULL;
   if (B < 1 || T < 0 || !conv_dims_ok(D) || B > ((int64_t)1 << 24) || T > ((int64_t)1 << 40))
     return GLA_ERR_SHAPE;
-  if (gla::conv_fwd_blocks(B, T, D) > (int64_t)0xFFFFFFFF) return GLA_ERR_SHAPE;
+  if (gla::conv_fwd_blocks(B, T, D) > (int64_t)0xFFFFFFFF / gla::conv_block_threads()) return GLA_ERR_SHAPE;
   gla_status st;
   if (T > 0) {
     if ((st = check_act(x, B, T, D)) != GLA_OK) return st;
@@ -452,7 +460,7 @@ gla_status gla_conv1d_step(int64_t N, int64_t D, const gla_tensor* x, const floa
                            float* state, int64_t state_stride_n, gla_tensor* y, void* stream) {
   if (!x || !w || !state || !y) return GLA_ERR_NULL;
   if (N < 1 || !conv_dims_ok(D) || N > ((int64_t)1 << 30)) return GLA_ERR_SHAPE;
-  if (gla::conv_step_blocks(N, D) > (int64_t)0xFFFFFFFF) return GLA_ERR_SHAPE;
+  if (gla::conv_step_blocks(N, D) > (int64_t)0xFFFFFFFF / gla::conv_block_threads()) return GLA_ERR_SHAPE;
   if (state_stride_n < (GLA_CONV_WIDTH - 1) * D) return GLA_ERR_SHAPE;
   gla_status st;
   if ((st = check_act(x, N, 1, D)) != GLA_OK) return st;

@@ -246,6 +246,7 @@ int64_t conv_fwd_blocks(int64_t B, int64_t T, int64_t D) {
 }
 
 int64_t conv_step_blocks(int64_t N, int64_t D) { return N * ((D / 8 + CTHR - 1) / CTHR); }
+int conv_block_threads() { return CTHR; }
 
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)conv_fwd_blocks(a.B, a.T, a.D)), block(CTHR);

@@ -133,8 +133,10 @@ hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
 bool decode_supported(int dk, int dv);
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);
 hipError_t launch_conv_step(const ConvStepArgs& a, hipStream_t st);
-// one-dimensional grid sizes of the two convolution launches
+// one-dimensional grid sizes of the two convolution launches, and their
+// workgroup size
 int64_t conv_fwd_blocks(int64_t B, int64_t T, int64_t D);
 int64_t conv_step_blocks(int64_t N, int64_t D);
+int conv_block_threads();
 
 }  // namespace gla

@@ -49,6 +49,9 @@
  *               chunk <= 32 for the backward.  Other combinations return
  *               GLA_ERR_UNSUPPORTED.  B, H >= 1; T >= 0 (T = 0 copies the
  *               state through); T need not be a multiple of chunk.
+ *               B <= 2^24, H <= 2^16, B * H <= 2^21 and T <= 2^40
+ *               (GLA_ERR_SHAPE otherwise): one launch addresses at most
+ *               2^32 - 1 work-items.
  *   Decay       lambda[h] must satisfy 0 <= lambda[h] <= 1 (not checked on
  *               the device); 0^0 is taken as 1.  NaN/Inf inputs propagate.
  *   Aliasing    Outputs must not share a base pointer with any input or with
@@ -146,7 +149,8 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
  *                                 over n, stride_h over h (stride_t unused)
  *   S    fp32, sequence n / head h at S + n*S_stride_n + h*dk*dv, dense
  *        dk x dv per head; S_stride_n >= H*dk*dv elements (a per-sequence
- *        page may hold further layers' states), 16-byte aligned. */
+ *        page may hold further layers' states), 16-byte aligned.
+ *   N, H >= 1, N * H <= 2^24 (GLA_ERR_SHAPE otherwise). */
 gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
                            const gla_tensor* k, const gla_tensor* v, const float* lambda,
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream);
@@ -204,6 +208,7 @@ gla_status gla_decode_step_fused(int64_t N, int64_t H, int64_t dk, int64_t dv, c
  *          are skipped (nothing read or written for them).
  *   has_state  device int32 [N] or NULL: the sequence starts from its page's
  *          state when nonzero (NULL: every sequence does), else from zero.
+ *   N, H >= 1, N * H <= 2^21, total_T < 2^31 (GLA_ERR_SHAPE otherwise).
  *          The final state is written back to the page (in place).
  * No workspace.  Slots must be distinct (two sequences writing one page
  * race). */
@@ -227,7 +232,9 @@ gla_status gla_chunk_fwd_varlen(int64_t N, int64_t H, int64_t total_T, int64_t d
  *   x, y      gla_tensor views of [B, T, D]: element (b, t, c) at
  *             data + b*stride_b + t*stride_t + c (stride_h unused); bf16 or
  *             fp32 each; 16-byte aligned rows, stride_t >= D
- *   D         multiple of 8, >= 8
+ *   D         multiple of 8, 8 <= D <= 2^24; a call's launch must stay below
+ *             2^32 work-items (one per 8 channels of 16 tokens, or of one
+ *             token in the decode step; GLA_ERR_SHAPE otherwise)
  *   w         fp32 [D][4];  bias fp32 [D] or NULL
  *   windows   fp32 [B][3][D], 16-byte aligned
  * ------------------------------------------------------------------------ */

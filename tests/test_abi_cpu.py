@@ -337,3 +337,31 @@ def test_fused_entry_points_reject_bad_arguments(lib):
     assert dec(gg=None) == NULL
     assert dec(aug=None) == NULL
     assert dec(y=T(0x500000, sb=2 * 192, sh=192)) == ALIAS
+
+
+# ------------------------------------------------------------ launch-size limits
+def test_launch_size_limits(lib):
+    """Every launch stays below 2^32 work-items: B*H (and N*H for the packed
+    prefill) at most 2^21, N*H at most 2^24 for decode, and the convolution's
+    work-item count is checked; the calls are rejected before any launch."""
+    ref = ctypes.byref
+    q, k, v, o = views()
+    # chunked forward: B*H = 2^21 + 2^10 is rejected (H = 2^10, B = 2^11 + 1)
+    assert fwd(lib, dims(B=(1 << 11) + 1, H=1 << 10), q, k, v, o) == SHAPE
+    # decode: N*H = 2^24 + 16
+    dq_, dk_, dv_, do_ = dec_views()
+    assert dec(lib, (1 << 20) + 1, 16, 96, 192, dq_, dk_, dv_, o=do_) == SHAPE
+    # packed prefill: N*H = 2^21 + 2^10
+    tq = gb.GlaTensor(0x100000, gb.GLA_BF16, 0, 96, 1024 * 96)
+    tk = gb.GlaTensor(0x200000, gb.GLA_BF16, 0, 96, 1024 * 96)
+    tv = gb.GlaTensor(0x300000, gb.GLA_BF16, 0, 192, 1024 * 192)
+    to = gb.GlaTensor(0x400000, gb.GLA_BF16, 0, 192, 1024 * 192)
+    assert lib.gla_chunk_fwd_varlen((1 << 11) + 1, 1024, 100, 96, 192, 64, ref(tq), ref(tk), ref(tv), 0x700000,
+                                    0x9000, 0x800000, 8, 1024 * 96 * 192, None, None, ref(to), None) == SHAPE
+    # convolution: 2^16 sequences of 2^16 tokens, 64 channels: 2^28 workgroups
+    # (fewer than 2^32) but more than 2^32 work-items
+    x, y = act(0x100000), act(0x200000)
+    assert conv_fwd(lib, 1 << 16, 1 << 16, 64, x, y) == SHAPE
+    # conv decode step: 2^24 sequences of 2^15 channels: 2^30 workgroups
+    xs, ys = T_(0x100000, gb.GLA_BF16, 1 << 15, 0), T_(0x200000, gb.GLA_BF16, 1 << 15, 0)
+    assert lib.gla_conv1d_step(1 << 24, 1 << 15, ref(xs), 0xA000, None, 0xC000, 3 << 15, ref(ys), None) == SHAPE
