@@ -174,11 +174,30 @@ def _check(lib, status):
         raise GlaError(status, lib.gla_status_string(status).decode())
 
 
-def _state_ok(S, B, H, dk, dv, name):
-    if S is None:
+def _expect(t, shape, name, dtype=None, contiguous=False):
+    """Shape (and optionally dtype / contiguity) of an argument: the C ABI sees
+    only pointers and strides, so extents are checked here."""
+    if t is None:
         return
-    if S.dtype != torch.float32 or tuple(S.shape) != (B, H, dk, dv) or not S.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {(B, H, dk, dv)}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(*tensors):
+    """Every tensor must live on one GPU: the kernels dereference the pointers."""
+    ts = [t for t in tensors if t is not None]
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"every tensor must be on the same GPU device (got {t.device} and {dev})")
+
+
+def _state_ok(S, B, H, dk, dv, name):
+    _expect(S, (B, H, dk, dv), name, torch.float32, contiguous=True)
 
 
 def chunk_fwd(q, k, v, lam, S0=None, chunk=64, out_dtype=None, o=None, S_T=None,
@@ -191,7 +210,13 @@ def chunk_fwd(q, k, v, lam, S0=None, chunk=64, out_dtype=None, o=None, S_T=None,
     lib = load_library()
     B, H, T, dk = q.shape
     dv = v.shape[-1]
+    _expect(k, (B, H, T, dk), "k")
+    _expect(v, (B, H, T, dv), "v")
+    _expect(lam, (H,), "lam", torch.float32, contiguous=True)
+    _expect(o, (B, H, T, dv), "o")
     _state_ok(S0, B, H, dk, dv, "S0")
+    _state_ok(S_T, B, H, dk, dv, "S_T")
+    _same_device(q, k, v, lam, o, S0, S_T)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=out_dtype or q.dtype, device=q.device)
     if S_T is None and return_state:
@@ -214,8 +239,16 @@ def chunk_bwd(q, k, v, lam, dO, S0=None, dS_T=None, chunk=64, grad_dtype=None,
     lib = load_library()
     B, H, T, DK = q.shape
     DV = v.shape[-1]
+    _expect(k, (B, H, T, DK), "k")
+    _expect(v, (B, H, T, DV), "v")
+    _expect(dO, (B, H, T, DV), "dO")
+    _expect(lam, (H,), "lam", torch.float32, contiguous=True)
+    for name, t, d in (("dq", dq, DK), ("dk", dk, DK), ("dv", dv, DV)):
+        _expect(t, (B, H, T, d), name)
     _state_ok(S0, B, H, DK, DV, "S0")
     _state_ok(dS_T, B, H, DK, DV, "dS_T")
+    _state_ok(dS0, B, H, DK, DV, "dS0")
+    _same_device(q, k, v, dO, lam, dq, dk, dv, S0, dS_T, dS0)
     gd = grad_dtype or q.dtype
     if dq is None:
         dq = torch.empty((B, H, T, DK), dtype=gd, device=q.device)
@@ -247,10 +280,15 @@ def decode_step_(q, k, v, lam, S, o=None, out_dtype=None):
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _expect(k, (N, H, dk), "k")
+    _expect(v, (N, H, dv), "v")
+    _expect(lam, (H,), "lam", torch.float32, contiguous=True)
+    _expect(o, (N, H, dv), "o")
     if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dk, dv):
         raise ValueError("S must be float32 of shape (N, H, dk, dv)")
     if S.stride()[1:] != (dk * dv, dv, 1):
         raise ValueError("each sequence's heads must be dense in S")
+    _same_device(q, k, v, lam, S, o)
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype or q.dtype, device=q.device)
     tq, tk, tv, to = _view3(q), _view3(k), _view3(v), _view3(o)
@@ -271,10 +309,17 @@ def chunk_fwd_fused(q, k, v, lam, g, aug, gamma, eps=1e-6, S0=None, chunk=64, ou
     lib = load_library()
     B, H, T, dk = q.shape
     dv = v.shape[-1]
+    _expect(k, (B, H, T, dk), "k")
+    _expect(v, (B, H, T, dv), "v")
+    _expect(g, (B, H, T, dv), "g")
+    _expect(lam, (H,), "lam", torch.float32, contiguous=True)
+    _expect(y, (B, H, T, dv), "y")
     _state_ok(S0, B, H, dk, dv, "S0")
+    _state_ok(S_T, B, H, dk, dv, "S_T")
     for name, t, shp in (("aug", aug, (H, dk)), ("gamma", gamma, (H, dv))):
         if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shp}")
+    _same_device(q, k, v, g, lam, y, S0, S_T, aug, gamma)
     if y is None:
         y = torch.empty((B, H, T, dv), dtype=out_dtype or q.dtype, device=q.device)
     if S_T is None and return_state:
@@ -305,6 +350,12 @@ def decode_step_fused_(q, k, v, lam, S, g, aug, gamma, eps=1e-6, y=None, out_dty
     for name, t, shp in (("aug", aug, (H, dk)), ("gamma", gamma, (H, dv))):
         if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shp}")
+    _expect(k, (N, H, dk), "k")
+    _expect(v, (N, H, dv), "v")
+    _expect(g, (N, H, dv), "g")
+    _expect(lam, (H,), "lam", torch.float32, contiguous=True)
+    _expect(y, (N, H, dv), "y")
+    _same_device(q, k, v, g, lam, S, y, aug, gamma)
     if y is None:
         y = torch.empty((N, H, dv), dtype=out_dtype or q.dtype, device=q.device)
     tq, tk, tv, tg, ty = _view3(q), _view3(k), _view3(v), _view3(g), _view3(y)
@@ -347,6 +398,13 @@ def chunk_fwd_varlen(q, k, v, lam, cu_seqlens, pool, slots=None, has_state=None,
     for name, t in (("slots", slots), ("has_state", has_state)):
         if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (N,)):
             raise ValueError(f"{name} must be int32 of shape ({N},)")
+    _expect(k, (total_T, H, dk), "k")
+    _expect(v, (total_T, H, dv), "v")
+    _expect(lam, (H,), "lam", torch.float32, contiguous=True)
+    _expect(o, (total_T, H, dv), "o")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    _same_device(q, k, v, lam, cu_seqlens, pool, slots, has_state, o)
     if o is None:
         o = torch.empty((total_T, H, dv), dtype=out_dtype or q.dtype, device=q.device)
     tq, tk, tv, to = _packed(q), _packed(k), _packed(v), _packed(o)
@@ -377,8 +435,9 @@ def _act3(x):
 def _conv_w_ok(w, bias, D):
     if w.dtype != torch.float32 or tuple(w.shape) != (D, CONV_WIDTH) or not w.is_contiguous():
         raise ValueError(f"w must be a contiguous float32 tensor of shape {(D, CONV_WIDTH)}")
-    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (D,)):
-        raise ValueError(f"bias must be float32 of shape {(D,)}")
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (D,)
+                             or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous float32 tensor of shape {(D,)}")
 
 
 def conv1d_fwd(x, w, bias=None, state_in=None, out_dtype=None, y=None, state_out=None,
@@ -388,10 +447,12 @@ def conv1d_fwd(x, w, bias=None, state_in=None, out_dtype=None, y=None, state_out
     lib = load_library()
     B, T, D = x.shape
     _conv_w_ok(w, bias, D)
+    _expect(y, (B, T, D), "y")
     for name, st_ in (("state_in", state_in), ("state_out", state_out)):
         if st_ is not None and (st_.dtype != torch.float32 or tuple(st_.shape) != (B, CONV_WIDTH - 1, D)
                                 or not st_.is_contiguous()):
             raise ValueError(f"{name} must be contiguous float32 of shape {(B, CONV_WIDTH - 1, D)}")
+    _same_device(x, w, bias, state_in, state_out, y)
     if y is None:
         y = torch.empty((B, T, D), dtype=out_dtype or x.dtype, device=x.device)
     if state_out is None and return_state:
@@ -414,6 +475,8 @@ def conv1d_step_(x, w, bias, state, y=None, out_dtype=None):
         raise ValueError(f"state must be float32 of shape {(N, CONV_WIDTH - 1, D)}")
     if state.stride()[1:] != (D, 1):
         raise ValueError("each sequence's window must be dense in state")
+    _expect(y, (N, D), "y")
+    _same_device(x, w, bias, state, y)
     if y is None:
         y = torch.empty((N, D), dtype=out_dtype or x.dtype, device=x.device)
     if x.stride(-1) != 1 or y.stride(-1) != 1:
