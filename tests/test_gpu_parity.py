@@ -389,3 +389,55 @@ def test_decode_equals_chunked_long_context_full(gla):
     flush("test_decode_equals_chunked_long_context_full T=65536")
     x = inputs.make_chunk_inputs("long")
     _check_decode_equivalence(gla, x)
+
+
+def test_decode_full_batch_sampled(gla):
+    """The batched-decode workload in the launch configuration the benchmark
+    times: a (24, 1280, 16, 96, 192) fp32 state pool (~9 GB), one layer slab
+    per call, q/k/v as strided views of one packed bf16 block per (step,
+    layer), bf16 output.  Two steps on the first and the last layer.  Each
+    call is repeated with fp32 output on a copy of the slab: the two state
+    updates must agree bit for bit, the bf16 output must be the fp32 output
+    rounded to nearest (within one bf16 ulp), and for 12 sampled (sequence,
+    head) pairs the fp32 output and the state must match the oracle to 1e-5.
+    Every other layer's slab must be untouched."""
+    flush("test_decode_full_batch_sampled N=1280 layers=24 H=16")
+    Lyr, N, H, dk, dv, steps = 24, 1280, 16, 96, 192, 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5_000_101)
+    S = torch.empty((Lyr, N, H, dk, dv), dtype=torch.float32, device="cuda")
+    S.normal_(0.0, 0.01, generator=g)
+    qkv = torch.randn((steps, 2, N, H, dk + dk + dv), generator=g, device="cuda").to(torch.bfloat16)
+    lam_h = np.asarray(inputs.lambda_log_spaced(H, 0.95, 0.9999), dtype=np.float32)
+    lam = dev_f32(lam_h)
+    rng = np.random.default_rng(7)
+    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, N, 12), rng.integers(0, H, 12))]
+    layers = (0, Lyr - 1)
+    # the sampled states before the first step, and one untouched layer
+    ref_S = {(ly, n, h): host(S[ly, n, h]) for ly in layers for n, h in pairs}
+    mid_before = host(S[Lyr // 2, :4])
+    o16 = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
+    for st in range(steps):
+        for li, ly in enumerate(layers):
+            blk = qkv[st, li]
+            qv, kv, vv = blk[..., :dk], blk[..., dk:2 * dk], blk[..., 2 * dk:]
+            S_copy = S[ly].clone()
+            gla.decode_step_(qv, kv, vv, lam, S[ly], o=o16)
+            o32 = gla.decode_step_(qv, kv, vv, lam, S_copy, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(S[ly], S_copy), (st, ly)
+            a = o16.view(torch.int16).cpu().numpy().astype(np.int32)
+            b = o32.to(torch.bfloat16).view(torch.int16).cpu().numpy().astype(np.int32)
+            assert np.max(np.abs(a - b)) <= 1, (st, ly)
+            del S_copy
+            got_o, bh = host(o32), host(blk)
+            for n, h in pairs:
+                q1, k1, v1 = bh[n, h, :dk], bh[n, h, dk:2 * dk], bh[n, h, 2 * dk:]
+                ro, rS = oracle.decode_step(q1[None, None], k1[None, None], v1[None, None], lam_h[h:h + 1],
+                                            ref_S[(ly, n, h)][None, None])
+                ref_S[(ly, n, h)] = rS[0, 0]
+                assert oracle.rel_err(got_o[n, h], ro[0, 0]) <= 1e-5, (st, ly, n, h)
+    for ly in layers:
+        for n, h in pairs:
+            assert oracle.rel_err(host(S[ly, n, h]), ref_S[(ly, n, h)]) <= 1e-5, (ly, n, h)
+    assert np.array_equal(host(S[Lyr // 2, :4]), mid_before)
