@@ -196,47 +196,64 @@ __global__ void __launch_bounds__(CTHR) conv_fwd_kernel(ConvArgs a) {
   }
 }
 
-// block id = n * channel blocks + channel block; one token per sequence,
-// window updated in place
+// block id = sequence group * channel blocks + channel block; one token per
+// sequence, window updated in place.  A thread serves SQ sequences of its 8
+// channels so that their taps are loaded once: the windows and inputs (from
+// HBM) are issued first, the taps (from L2) after them.
+constexpr int SQ = 4;
+
 template <bool IN_F32, bool OUT_F32>
 __global__ void __launch_bounds__(CTHR) conv_step_kernel(ConvStepArgs a) {
   const int64_t cblocks = (a.D / 8 + CTHR - 1) / CTHR;
-  const int64_t n = blockIdx.x / cblocks;
+  const int64_t n0 = (blockIdx.x / cblocks) * SQ;
   const int64_t c0 = ((blockIdx.x % cblocks) * CTHR + threadIdx.x) * 8;
   if (c0 >= a.D) return;
-  float wt[CW][8], bs[8];
-  load_taps(a.w, a.bias, c0, wt, bs);
-  float* win = a.state + n * a.state_stride_n;
-  float h[CW - 1][8], xv[8];
+  float h[SQ][CW - 1][8], xv[SQ][8];
 #pragma unroll
-  for (int j = 0; j < CW - 1; ++j) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(win + j * a.D + c0);
-    const f32x4 u = p[0], v = p[1];
+  for (int i = 0; i < SQ; ++i) {
+    const int64_t n = n0 + i;
+    if (n < a.N) {
+      const float* win = a.state + n * a.state_stride_n;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[j][e] = u[e];
-      h[j][4 + e] = v[e];
+      for (int j = 0; j < CW - 1; ++j) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(win + j * a.D + c0);
+        const f32x4 u = p[0], v = p[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[i][j][e] = u[e];
+          h[i][j][4 + e] = v[e];
+        }
+      }
+      load8<IN_F32>(a.x, n * a.sx_n + c0, xv[i]);
     }
   }
-  load8<IN_F32>(a.x, n * a.sx_n + c0, xv);
-  float yv[8];
+  float wt[CW][8], bs[8];
+  load_taps(a.w, a.bias, c0, wt, bs);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float z = bs[e];
-    z = fmaf(wt[0][e], h[0][e], z);
-    z = fmaf(wt[1][e], h[1][e], z);
-    z = fmaf(wt[2][e], h[2][e], z);
-    z = fmaf(wt[3][e], xv[e], z);
-    yv[e] = silu(z);
-  }
-  store8<OUT_F32>(a.y, n * a.sy_n + c0, yv);
-  // drop the oldest input, append this token
+  for (int i = 0; i < SQ; ++i) {
+    const int64_t n = n0 + i;
+    if (n < a.N) {
+      float yv[8];
 #pragma unroll
-  for (int j = 0; j < CW - 1; ++j) {
-    const float* src = j + 1 < CW - 1 ? h[j + 1] : xv;
-    f32x4* p = reinterpret_cast<f32x4*>(win + j * a.D + c0);
-    p[0] = f32x4{src[0], src[1], src[2], src[3]};
-    p[1] = f32x4{src[4], src[5], src[6], src[7]};
+      for (int e = 0; e < 8; ++e) {
+        float z = bs[e];
+        z = fmaf(wt[0][e], h[i][0][e], z);
+        z = fmaf(wt[1][e], h[i][1][e], z);
+        z = fmaf(wt[2][e], h[i][2][e], z);
+        z = fmaf(wt[3][e], xv[i][e], z);
+        yv[e] = silu(z);
+      }
+      store8<OUT_F32>(a.y, n * a.sy_n + c0, yv);
+      // drop the oldest input, append this token
+      float* win = a.state + n * a.state_stride_n;
+#pragma unroll
+      for (int j = 0; j < CW - 1; ++j) {
+        const float* src = j + 1 < CW - 1 ? h[i][j + 1] : xv[i];
+        f32x4* p = reinterpret_cast<f32x4*>(win + j * a.D + c0);
+        p[0] = f32x4{src[0], src[1], src[2], src[3]};
+        p[1] = f32x4{src[4], src[5], src[6], src[7]};
+      }
+    }
   }
 }
 
@@ -245,7 +262,7 @@ int64_t conv_fwd_blocks(int64_t B, int64_t T, int64_t D) {
   return B * runs * ((D / 8 + CTHR - 1) / CTHR);
 }
 
-int64_t conv_step_blocks(int64_t N, int64_t D) { return N * ((D / 8 + CTHR - 1) / CTHR); }
+int64_t conv_step_blocks(int64_t N, int64_t D) { return (N + SQ - 1) / SQ * ((D / 8 + CTHR - 1) / CTHR); }
 int conv_block_threads() { return CTHR; }
 
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st) {
