@@ -441,3 +441,37 @@ def test_decode_full_batch_sampled(gla):
         for n, h in pairs:
             assert oracle.rel_err(host(S[ly, n, h]), ref_S[(ly, n, h)]) <= 1e-5, (ly, n, h)
     assert np.array_equal(host(S[Lyr // 2, :4]), mid_before)
+
+
+def test_fwd_bwd_max_units(gla):
+    """The largest launch the ABI accepts: B*H = 2^21 (b, h) units, here
+    B = 131,072 sequences of T = 2 tokens (bf16, dk=96, dv=192, chunk 64, no
+    state tensors).  The forward launches 2^22 workgroups and the backward's
+    paired launch 2^22 as well (1.6e9 work-items each); sampled heads,
+    including the last one, match the oracle."""
+    flush("test_fwd_bwd_max_units B=131072 H=16 T=2")
+    B, H, T, dk, dv = 1 << 17, 16, 2, 96, 192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5_000_202)
+    q = torch.randn((B, H, T, dk), generator=g, device="cuda").to(torch.bfloat16)
+    k = (torch.randn((B, H, T, dk), generator=g, device="cuda") / dk ** 0.5).to(torch.bfloat16)
+    v = torch.randn((B, H, T, dv), generator=g, device="cuda").to(torch.bfloat16)
+    dO = torch.randn((B, H, T, dv), generator=g, device="cuda").to(torch.bfloat16)
+    lam_h = np.asarray(inputs.lambda_log_spaced(H, 0.9, 0.999), dtype=np.float32)
+    lam = dev_f32(lam_h)
+    o, _ = gla.chunk_fwd(q, k, v, lam, None, chunk=64, out_dtype=torch.float32, return_state=False)
+    dq, dk_, dv_, _ = gla.chunk_bwd(q, k, v, lam, dO, None, None, chunk=64, grad_dtype=torch.float32,
+                                    need_dS0=False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    samples = [(B - 1, H - 1), (0, 0)] + [(int(b), int(h)) for b, h in
+                                           zip(rng.integers(0, B, 6), rng.integers(0, H, 6))]
+    for b, h in samples:
+        sl = lambda t: host(t[b:b + 1, h:h + 1])
+        qs, ks, vs, dOs = sl(q), sl(k), sl(v), sl(dO)
+        lh = lam_h[h:h + 1]
+        ro, _ = oracle.fwd(qs, ks, vs, lh)
+        rdq, rdk, rdv, _ = oracle.bwd(qs, ks, vs, lh, dOs)
+        assert oracle.rel_err(sl(o), ro) <= TOL["bf16"], (b, h)
+        for got, ref in ((dq, rdq), (dk_, rdk), (dv_, rdv)):
+            assert oracle.rel_err(sl(got), ref) <= TOL["bf16"], (b, h)
