@@ -365,3 +365,14 @@ def test_launch_size_limits(lib):
     # conv decode step: 2^24 sequences of 2^15 channels: 2^30 workgroups
     xs, ys = T_(0x100000, gb.GLA_BF16, 1 << 15, 0), T_(0x200000, gb.GLA_BF16, 1 << 15, 0)
     assert lib.gla_conv1d_step(1 << 24, 1 << 15, ref(xs), 0xA000, None, 0xC000, 3 << 15, ref(ys), None) == SHAPE
+
+
+def test_c_consumer_compiles():
+    """The plain-C consumer of include/gla.h builds with gcc against libgla.so
+    (it runs on the GPU in test_gpu_c_abi)."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("c_abi_build", os.path.join(REPO, "tests", "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert os.path.exists(mod.build())
