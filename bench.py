@@ -8,7 +8,8 @@ chunks (the same step at the pages' 128-token chunk is reported under
 same run also measures the batched decode workload (1,280 sequences x 24
 layers x 16 heads of fp32 96x192 states, 64 steps) and reports it under
 "decode", and times the fp64 CPU oracle on a bounded sample under
-"cpu_baseline".
+"cpu_baseline" (and beside the decode, convolution, packed-prefill and
+fused-epilogue rows under their "cpu_oracle" keys).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-decode] [--no-cpu]
                     [--decode-steps N] [--calibrate-copy]
@@ -405,6 +406,61 @@ def cpu_baseline(inputs, min_seconds=5.0):
                        f"T=2048, fp64 oracle), {dt:.2f} s wall")
 
 
+def _timed(fn, min_seconds):
+    """Calls fn until min_seconds of wall time have passed; (calls, seconds)."""
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return reps, dt
+
+
+def oracle_rows(inputs, min_seconds=0.5):
+    """The fp64 oracle timed beside the other rows, each on a bounded sample
+    of the row's own workload (same recipes), scaled to that row's unit."""
+    import numpy as np
+
+    import oracle
+
+    out = {}
+    # decode: one step of 64 of the 1,280 sequences (16 heads), per layer call
+    N, H = 64, 16
+    x = inputs.random_chunk_inputs(5_000_011, N, H, 1, DK, DV, dtype="bf16", scale=1.0)
+    S = inputs.normal(5_000_011, inputs.TID["S"], (N, H, DK, DV), 0.01, "f32")
+    q, k, v = (np.ascontiguousarray(x[n][:, :, 0]) for n in ("q", "k", "v"))
+    reps, dt = _timed(lambda: oracle.decode_step(q, k, v, x["lam"], S), min_seconds)
+    out["decode"] = dict(ms_per_layer_call=dt / reps * 1e3 * 1280 / N,
+                         sample=f"{reps} steps of {N} sequences x {H} heads, scaled to 1,280 sequences")
+    # convolution prefill: one of the 8 sequences (2,048 tokens x 3,072 channels)
+    c = inputs.conv_inputs(5_000_012, 1, 2048, 3072, "bf16", state=False)
+    reps, dt = _timed(lambda: oracle.conv1d(c["x"], c["w"], c["bias"]), min_seconds)
+    out["conv1d_prefill"] = dict(ms=dt / reps * 1e3 * 8, sample=f"{reps} calls on 1 of 8 sequences, scaled to 8")
+    # packed prefill: the forward recurrence of the first 4 prompts of the benched mix
+    cv = inputs.CONFIGS["varlen"]
+    lengths = inputs.varlen_lengths(cv["cid"], cv["N"], cv["min_len"], cv["max_len"])
+    sub = [int(t) for t in lengths[:4]]
+    xs = [inputs.random_chunk_inputs(5_000_013 + i, 1, cv["H"], t, DK, DV, dtype="bf16") for i, t in enumerate(sub)]
+    reps, dt = _timed(lambda: [oracle.fwd(a["q"], a["k"], a["v"], a["lam"], a["S0"]) for a in xs], min_seconds)
+    out["varlen_prefill"] = dict(tokens_per_s=reps * sum(sub) / dt,
+                                 sample=f"{reps} passes over 4 prompts ({sum(sub)} tokens, 16 heads)")
+    # fused epilogue: forward + epilogue on a 256-token slice of one training sequence
+    xe = inputs.random_chunk_inputs(5_000_014, 1, 16, 256, DK, DV, dtype="bf16")
+    e = inputs.epilogue_inputs(5_000_014, 1, 16, 256, DK, DV, "bf16", aug_scale=0.1)
+
+    def fused():
+        o, _ = oracle.fwd(xe["q"], xe["k"], xe["v"], xe["lam"], xe["S0"])
+        oracle.epilogue(xe["q"], xe["k"], xe["v"], o, e["aug"], e["gamma"], 1e-6, e["g"])
+
+    reps, dt = _timed(fused, min_seconds)
+    out["fused_epilogue_fwd"] = dict(tokens_per_s=reps * 256 / dt, sample=f"{reps} passes over 256 tokens, 16 heads")
+    for row in out.values():
+        row.update(kind="oracle", cores=oracle.num_threads())
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +521,13 @@ def main():
         log("bench: cpu oracle baseline")
         cpu = cpu_baseline(inputs)
         log(f"  {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+        log("bench: cpu oracle beside the other rows")
+        rows = oracle_rows(inputs)
+        for key, target in (("decode", dec), ("conv1d_prefill", extra["conv1d"]["prefill"]),
+                            ("varlen_prefill", extra["varlen_prefill"]),
+                            ("fused_epilogue_fwd", extra["fused_epilogue_fwd"])):
+            if target is not None:
+                target["cpu_oracle"] = rows[key]
 
     # dominant kernel: the longer of the forward launch and the backward call
     fwd_gbs = tr["fwd_bytes"] / (tr["ms_fwd"] / 1e3) / 1e9
