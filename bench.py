@@ -473,8 +473,9 @@ def main():
                     help="also run a plain 1 GiB device copy (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the hot path shards over (b, h) and sequences with no communication, see DESIGN.md)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every call works on "
+              "one device; the hot path would shard over (b, h) units and sequences with no "
+              "communication between devices)",
               file=sys.stderr)
         sys.exit(2)
 
