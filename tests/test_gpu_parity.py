@@ -74,6 +74,17 @@ def test_fwd_fp32_full_head_dims(gla, chunk):
     check_fwd(gla, x, "f32", chunk)
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_bwd_fp32_full_head_dims(gla, chunk):
+    """fp32 backward at dk=96, dv=192 (the transposed passes' three-plane
+    kernels), ragged T with dS_T; the small batch also takes the segment
+    split."""
+    flush(f"test_bwd_fp32_full_head_dims chunk={chunk}")
+    x = inputs.random_chunk_inputs(135, 1, 2, 150, 96, 192, dtype="f32", dS_T=True)
+    assert segments_of(gla, 1, 2, 150, 96, 192, chunk, bwd=True) >= 2
+    check_bwd(gla, x, "f32", chunk)
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128])
 def test_fwd_bf16_chunk_invariance(gla, chunk):
     """Same bf16 inputs (Laplace recipe, 4 heads, ragged T) at every chunk."""
