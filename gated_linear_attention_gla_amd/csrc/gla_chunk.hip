@@ -456,9 +456,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   TileStager<NT, CP, DK, DKP, PQ, NTHR> pfq;
   TileStager<NT, CP, DK, DKP, PK, NTHR> pfk;
   TileStager<NT, CP, BN, BN, PVV, NTHR> pfv;
-  // With wide query/key rows the three prefetched tiles do not fit in
-  // registers next to the state, the P tile and the readout; the next query
-  // tile is then fetched only after stage 2 (the register peak).
+  // With wide query/key rows (192 channels) the next query tile is fetched
+  // only after stage 2: holding it through the P tiles and the readout keeps
+  // 16 more registers live at the register peak, and the earlier fetch
+  // measured slower.
   constexpr bool LATE_Q = DK > 128;
   auto prefetch_q = [&](int64_t ci) {
     const int64_t t0 = chunk_start(ci);
