@@ -69,8 +69,10 @@ template <> struct Raw8<3> { f32x4 a, b; };
 // multiple of the vectors per row, its column is fixed and its rows step by
 // RPJ.  Loads go through a buffer resource whose size ends at the last valid
 // row, so rows >= L read as zero without branches; columns in [COLS, COLSP)
-// are zero.  LDS holds NT bf16 planes with row pitch PITCH.
-template <int NT, int ROWS, int COLS, int COLSP, int PITCH, int NTHR>
+// are zero.  LDS holds NT bf16 planes with row pitch PITCH.  With SWZ, rows
+// whose bit 3 is set hold their 16-column groups pairwise exchanged (column c
+// at c ^ 16), the layout the readers of such tiles assume (tile_swz).
+template <int NT, int ROWS, int COLS, int COLSP, int PITCH, int NTHR, bool SWZ = false>
 struct TileStager {
   static constexpr int VPR = COLSP / 8;
   static_assert(NTHR % VPR == 0, "threads must cover whole rows");
@@ -78,6 +80,7 @@ struct TileStager {
   static constexpr int NPER = (ROWS + RPJ - 1) / RPJ;
   static constexpr int PLANE = ROWS * PITCH;
   static constexpr int ES = NT == 1 ? 2 : 4;  // input element size
+  static_assert(!SWZ || COLSP % 32 == 0, "the swizzle exchanges 16-column groups within 32");
   Raw8<NT> r[NPER];
 
   // gsrc: the tile's first row; row_stride in elements; L valid rows (>= 1)
@@ -117,7 +120,7 @@ struct TileStager {
     for (int j = 0; j < NPER; ++j) {
       const int row = row0 + j * RPJ;
       if (ROWS % RPJ == 0 || row < ROWS) {
-        bf16_t* dst = lds + row * PITCH + c;
+        bf16_t* dst = lds + row * PITCH + (SWZ ? c ^ ((row & 8) << 1) : c);
         if constexpr (NT == 1) {
           *reinterpret_cast<bf16x8*>(dst) = r[j].v;
         } else {
@@ -164,6 +167,16 @@ constexpr int pitch_kt(int dkp) {
     if ((2 * p) % 256 == 192) return p;
 }
 
+// Column swizzle of the key and value tiles (64 or more columns, a multiple of
+// 32): row r keeps column c at c ^ tile_swz(r).  At a byte pitch of 192 mod
+// 256, rows r and r + 8 of a transposing column read otherwise hit the same
+// banks; exchanging the 16-column groups of rows with bit 3 set makes those
+// reads and the 16-byte row reads of the key tile conflict-free (measured with
+// rocprofv3 SQ_LDS_BANK_CONFLICT per access pattern on gfx950).  Every access
+// keeps 8-element groups whole, so 16-byte stores and reads are unchanged.
+constexpr bool tile_swizzled(int cols) { return cols >= 64 && cols % 32 == 0; }
+__device__ __forceinline__ int tile_swz(int row) { return (row & 8) << 1; }
+
 // State row held in accumulator slot r of row tile D by lane group g.  With DK
 // a multiple of 32 the two tiles of each 32-row block interleave in runs of 4
 // (tile 2m + h, group g: rows 32 m + 8 g + 4 h + r), so the 8 k-slots a lane
@@ -190,8 +203,12 @@ struct ChunkLds {
   // tile mostly with column reads (pitch_kt), the value tile with column reads
   // (the same cost at any pitch).
   static constexpr int PQ = DKP >= 32 ? pitch_p(DKP - 8) : DKP + 8;
+  // key / value tiles swizzled (tile_swz); not at 128-token chunks or with fp32
+  // inputs, where the per-lane column arithmetic would spill registers
+  static constexpr bool SWK = NT == 1 && CP <= 64 && tile_swizzled(DKP);
+  static constexpr bool SWV = NT == 1 && CP <= 64 && tile_swizzled(BN);
   static constexpr int PK = pitch_kt(DKP);
-  static constexpr int PVV = BN + 16;
+  static constexpr int PVV = SWV ? pitch_kt(BN) : BN + 16;
   static constexpr int PP = pitch_p(CP);
   static constexpr int Q_ELEMS = NT * CP * PQ;
   static constexpr int K_ELEMS = NT * CP * PK;
@@ -254,6 +271,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   constexpr int PQ = Lds::PQ;
   constexpr int PK = Lds::PK;
   constexpr int PVV = Lds::PVV;
+  constexpr bool SWK = Lds::SWK;
+  constexpr bool SWV = Lds::SWV;
   constexpr int PP = Lds::PP;
   constexpr int DKT = DK / 16;  // 16-row tiles of the state
   constexpr int KSD = DKP / 32;  // 32-deep k-steps over DK
@@ -454,8 +473,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // The next chunk's tiles are loaded into registers while the current chunk
   // is computed, so HBM latency overlaps the MFMA work.
   TileStager<NT, CP, DK, DKP, PQ, NTHR> pfq;
-  TileStager<NT, CP, DK, DKP, PK, NTHR> pfk;
-  TileStager<NT, CP, BN, BN, PVV, NTHR> pfv;
+  TileStager<NT, CP, DK, DKP, PK, NTHR, SWK> pfk;
+  TileStager<NT, CP, BN, BN, PVV, NTHR, SWV> pfv;
   // With wide query/key rows (192 channels) the next query tile is fetched
   // only after stage 2: holding it through the P tiles and the readout keeps
   // 16 more registers live at the register peak, and the earlier fetch
@@ -530,7 +549,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           for (int u = 0; u < TP; ++u)
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
-              A[u][p] = lds_read_b128(&sK[p * CP * PK + (16 * Ja[u] + li) * PK + 32 * ks + 8 * g]);
+              A[u][p] = lds_read_b128(&sK[p * CP * PK + (16 * Ja[u] + li) * PK + 32 * ks +
+                                          (SWK ? 8 * g ^ tile_swz(li) : 8 * g)]);
               Bq[u][p] = lds_read_b128(&sQ[p * CP * PQ + (16 * Ia[u] + li) * PQ + 32 * ks + 8 * g]);
             }
 #pragma unroll
@@ -651,7 +671,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
           qp[p] = lds_read_b128(&sQ[p * CP * PQ + row * PQ + part * 8]);
-          kp[p] = lds_read_b128(&sK[p * CP * PK + row * PK + part * 8]);
+          kp[p] = lds_read_b128(&sK[p * CP * PK + row * PK + (SWK ? part * 8 ^ tile_swz(row) : part * 8)]);
         }
         float sacc = 0.0f;
 #pragma unroll
@@ -691,7 +711,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       bf16x8 Bv[NS][NT];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int c0 = (w * NS + s) * 16 + 4 * (li & 3);
+        // rows 32 ks + 8 g + (0..7): bit 3 is that of 8 g
+        const int c0 = ((w * NS + s) * 16 + 4 * (li & 3)) ^ (SWV ? tile_swz(8 * g) : 0);
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
           const bf16_t* base = &sV[p * CP * PVV + (32 * ks + 8 * g + (li >> 2)) * PVV + c0];
@@ -739,7 +760,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         for (int p = 0; p < NT; ++p) {
           // lane li supplies the 4-column group that lanes 4 (li & 3) .. + 3
           // receive: their state rows (state_row) select the key columns
-          const int kc = DK % 32 == 0 ? 32 * (D >> 1) + 8 * (li & 3) + 4 * (D & 1) : 16 * D + 4 * (li & 3);
+          const int kc = (DK % 32 == 0 ? 32 * (D >> 1) + 8 * (li & 3) + 4 * (D & 1) : 16 * D + 4 * (li & 3)) ^
+                         (SWK ? tile_swz(8 * g) : 0);
           const bf16_t* base = &sK[p * CP * PK + (32 * ks + 8 * g + (li >> 2)) * PK + kc];
           Ak[p] = cat4(lds_read_tr(base), lds_read_tr(base + 4 * PK));
         }
@@ -773,7 +795,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           for (int r = 0; r < 4; ++r) vreg[I][s][r] = 0.0f;
 #pragma unroll
           for (int p = 0; p < NT; ++p) {
-            const bf16x4 t = lds_read_b64(&sV[p * CP * PVV + (16 * I + li) * PVV + (w * NS + s) * 16 + 4 * g]);
+            const bf16x4 t = lds_read_b64(&sV[p * CP * PVV + (16 * I + li) * PVV +
+                                              (((w * NS + s) * 16 + 4 * g) ^ (SWV ? tile_swz(li) : 0))]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) vreg[I][s][r] += bf16v_to_f32(t[r]);
           }
