@@ -285,6 +285,25 @@ def counted_traffic():
     return t.get("bwd_call_bytes")
 
 
+MFMA_FILE = os.path.join(REPO, "profiles", "chunk_kernels_training_mfma_lds.json")
+
+
+def counted_mfma():
+    """MFMA utilisation of the training kernels from the committed counter
+    summary (busy MFMA cycles over active cycles of all 1,024 SIMDs, i.e. the
+    executed bf16 MFMA flops over the dense peak), or None when it is missing
+    or was counted on other kernel sources."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return {k: t[k] for k in ("fwd_mfma_util", "bwd_mfma_util", "fwd_executed_over_algorithmic_flops",
+                              "bwd_executed_over_algorithmic_flops")}
+
+
 def bench_conv(gla, inputs, reps=50):
     """Depthwise causal conv + SiLU in front of the mixer: the training batch
     (B=8, T=2,048, D=3,072, bf16 in and out) and one decode step of 1,280
@@ -580,6 +599,7 @@ def main():
             "mfma_frac": step_flops / (tr["ms_step"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
             "attainable_frac": max(step_bytes / (HBM_PEAK_GBS * 1e9),
                                    step_flops / (BF16_PEAK_TFLOPS * 1e12)) / (tr["ms_step"] / 1e3),
+            "mfma_counted": counted_mfma(),
             "fwd_gbs": fwd_gbs, "bwd_gbs": bwd_gbs,
             "ms_fwd": tr["ms_fwd"], "ms_bwd": tr["ms_bwd"],
         },
