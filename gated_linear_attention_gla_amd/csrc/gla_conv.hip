@@ -65,17 +65,18 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[
   }
 }
 
+// outputs are not read again by these kernels: non-temporal stores
 template <bool F32>
 __device__ __forceinline__ void store8(void* base, int64_t off, const float (&v)[8]) {
   if constexpr (F32) {
     f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off);
-    p[0] = f32x4{v[0], v[1], v[2], v[3]};
-    p[1] = f32x4{v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, p);
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, p + 1);
   } else {
     bf16x8 a;
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = (__bf16)v[e];
-    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16_t*>(base) + off) = a;
+    __builtin_nontemporal_store(a, reinterpret_cast<bf16x8*>(reinterpret_cast<bf16_t*>(base) + off));
   }
 }
 
@@ -83,13 +84,14 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const float (&v)
 // z -> -inf the reciprocal of +inf is 0, so the result tends to -0.
 __device__ __forceinline__ float silu(float z) { return z * __frcp_rn(1.0f + __expf(-z)); }
 
-// taps of 8 channels: wt[j][e] = w[c0 + e][j]; the bias as two 16-byte
-// vectors (a lane's 8 biases are contiguous)
-__device__ __forceinline__ void load_taps(const float* w, const float* bias, int64_t c0, float (&wt)[CW][8],
+// taps of 8 channels: wt[j][e] = w[c0 + e][j] (one 16-byte vector per
+// channel, from global memory or from a workgroup's LDS copy); the bias as two
+// 16-byte vectors (a lane's 8 biases are contiguous)
+__device__ __forceinline__ void load_taps(const f32x4* w4, const float* bias, int64_t c0, float (&wt)[CW][8],
                                           float (&bs)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(w + (c0 + e) * CW);
+    const f32x4 t = w4[e];
 #pragma unroll
     for (int j = 0; j < CW; ++j) wt[j][e] = t[j];
   }
@@ -118,6 +120,20 @@ __global__ void __launch_bounds__(CTHR) conv_fwd_kernel(ConvArgs a) {
   const int64_t run = (bid / cblocks) % runs;
   const int64_t b = bid / (cblocks * runs);
   const int64_t c0 = (cb * CTHR + threadIdx.x) * 8;
+  // The block's taps are staged in LDS with coalesced loads: read directly,
+  // each lane's 128 contiguous bytes make every load instruction touch 64
+  // cache lines.  Every thread takes part, also those past the last channel.
+  __shared__ f32x4 sw[CTHR * 8];
+  {
+    const int64_t cbase = cb * CTHR * 8;
+    const f32x4* wsrc = reinterpret_cast<const f32x4*>(a.w) + cbase;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = k * CTHR + (int)threadIdx.x;
+      if (cbase + i < a.D) sw[i] = wsrc[i];
+    }
+  }
+  __syncthreads();
   if (c0 >= a.D) return;
   const int64_t t0 = run * CT;
   const int64_t t1 = (a.T - t0) < CT ? a.T : t0 + CT;
@@ -156,9 +172,8 @@ __global__ void __launch_bounds__(CTHR) conv_fwd_kernel(ConvArgs a) {
       if (t < t1) load_raw<IN_F32>(a.x, b * a.sx_b + t * a.sx_t + c0, dst[u]);
     }
   };
-  // the first rows go out before the taps: they come from HBM, the taps from L2
   load_group(0, xr[0]);
-  load_taps(a.w, a.bias, c0, wt, bs);
+  load_taps(sw + threadIdx.x * 8, a.bias, c0, wt, bs);
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     if (gi + 1 < G) load_group(gi + 1, xr[(gi + 1) & 1]);
@@ -228,7 +243,7 @@ __global__ void __launch_bounds__(CTHR) conv_step_kernel(ConvStepArgs a) {
     }
   }
   float wt[CW][8], bs[8];
-  load_taps(a.w, a.bias, c0, wt, bs);
+  load_taps(reinterpret_cast<const f32x4*>(a.w) + c0, a.bias, c0, wt, bs);
 #pragma unroll
   for (int i = 0; i < SQ; ++i) {
     const int64_t n = n0 + i;
