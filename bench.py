@@ -70,6 +70,23 @@ def event_time_ms(fn, n, stream):
     return s.elapsed_time(e) / n
 
 
+def warm_up(fn, min_seconds=0.05):
+    """Run fn until min_seconds of wall time have passed.  After the host has
+    generated a workload's inputs the GPU has been idle, and its clock takes
+    about 30 ms of sustained load to return to speed (measured: the training
+    forward runs 112-129 us for its first ~100 calls after a pause, then 99
+    us), so timing right away reads low."""
+    import torch
+
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= min_seconds:
+            return
+
+
 def bench_train(gla, inputs, steps, warmup, chunk=C):
     import numpy as np
     import torch
@@ -140,10 +157,7 @@ def bench_fwd_bwd_events(gla, inputs, name, reps, chunk=C):
     dq, dk, dv, dS0 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(S0)
     fwd = lambda: gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, o=o, S_T=S_T)
     bwd = lambda: gla.chunk_bwd(q, k, v, lam, dO, S0, None, chunk=chunk, dq=dq, dk=dk, dv=dv, dS0=dS0)
-    for _ in range(3):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
+    warm_up(lambda: (fwd(), bwd()))
     stream = torch.cuda.current_stream()
     ms_fwd = event_time_ms(fwd, reps, stream)
     ms_bwd = event_time_ms(bwd, reps, stream)
@@ -166,9 +180,7 @@ def bench_fwd_only(gla, inputs, name, reps, chunk=C):
     o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
     S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
     fn = lambda: gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, o=o, S_T=S_T)
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn)
     ms = event_time_ms(fn, reps, torch.cuda.current_stream())
     units = B * H * T
     nbytes = units * FWD_BYTES + (2 if S0 is not None else 1) * B * H * STATE_BYTES
@@ -204,8 +216,7 @@ def bench_decode(gla, inputs, steps_override=None):
     # warm up on a scratch copy of one slab so the timed steps start from the seeded states
     tmp = S[0].clone()
     blk = qkv[0, 0]
-    for _ in range(3):
-        gla.decode_step_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, tmp, o=o)
+    warm_up(lambda: gla.decode_step_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, tmp, o=o))
     del tmp
     stream = torch.cuda.current_stream()
     s = torch.cuda.Event(enable_timing=True)
@@ -225,8 +236,7 @@ def bench_decode(gla, inputs, steps_override=None):
     blk = qkv[0, 0]
     fused = lambda: gla.decode_step_fused_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, S[0], gz,
                                            aug, gam, 1e-6, y=o)
-    fused()
-    torch.cuda.synchronize()
+    warm_up(fused)
     fused_ms = event_time_ms(fused, 20, stream)
     return dict(
         workload="decode: 1280 seqs x 24 layers x H=16, fp32 96x192 states, 64 steps, bf16 q/k/v",
@@ -319,9 +329,7 @@ def bench_conv(gla, inputs, reps=50):
     y = torch.empty_like(x)
     st = torch.empty((B, 3, D), dtype=torch.float32, device="cuda")
     fwd = lambda: gla.conv1d_fwd(x, w, bias, None, y=y, state_out=st)
-    for _ in range(3):
-        fwd()
-    torch.cuda.synchronize()
+    warm_up(fwd)
     stream = torch.cuda.current_stream()
     ms = event_time_ms(fwd, reps, stream)
     nbytes = B * T * D * (2 + 2) + B * 3 * D * 4 + D * 5 * 4
@@ -330,9 +338,7 @@ def bench_conv(gla, inputs, reps=50):
     win = torch.randn((N, 3, D), device="cuda")
     ys = torch.empty_like(xs)
     step = lambda: gla.conv1d_step_(xs, w, bias, win, y=ys)
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step)
     ms_s = event_time_ms(step, reps, stream)
     sbytes = N * D * (2 + 2 + 2 * 3 * 4) + D * 5 * 4
     return dict(
@@ -361,9 +367,7 @@ def bench_fused(gla, inputs, reps=20):
     y = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
     S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
     fn = lambda: gla.chunk_fwd_fused(q, k, v, lam, g, aug, gamma, 1e-6, S0, chunk=C, y=y, S_T=S_T)
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn)
     ms = event_time_ms(fn, reps, torch.cuda.current_stream())
     nbytes = B * H * T * (FWD_BYTES + 2 * DV) + 2 * B * H * STATE_BYTES
     return dict(workload=f"fwd + fused output epilogue, B={B} H={H} T={T} chunk={C}, bf16 q/k/v/g/y",
@@ -390,9 +394,7 @@ def bench_varlen(gla, inputs, reps=20):
     total = int(lengths.sum())
     o = torch.empty((total, c["H"], c["dv"]), dtype=torch.bfloat16, device="cuda")
     fn = lambda: gla.chunk_fwd_varlen(q, k, v, lam, cu, pool, slots, has, chunk=C, o=o)
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn)
     ms = event_time_ms(fn, reps, torch.cuda.current_stream())
     units = total * c["H"]
     nbytes = units * FWD_BYTES + 2 * c["N"] * c["H"] * STATE_BYTES
@@ -484,7 +486,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 100 steps (~40 ms) also bring the GPU clock to speed (see warm_up)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None)
