@@ -521,22 +521,23 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 
     // ---------------- stage 1: masked P tiles (causal half), P[i][j] row-major
     // Each wave computes the tiles t = w, w + NW, ..., TP of them at a time so
-    // their LDS reads and MFMA chains overlap.  A slot past the last tile
-    // recomputes tile 0 and discards it, which keeps the code branch-free.
+    // their LDS reads and MFMA chains overlap.  Slots past the last tile are
+    // skipped (the wave index is uniform, so this is a scalar branch): when the
+    // tiles do not divide evenly the waves that run out are those after the
+    // first NPT % NW, i.e. the second waves on SIMDs 0 and 1, which carry the
+    // longest path through the chunk.
     f32x4 ptile[ALIAS_P ? MAXPT : 1];
     if constexpr (!SO) {
       constexpr int TP = (TIGHT || MAXPT < 2) ? 1 : 2;
+      auto p_batch = [&](auto tp_c, const int kt0) {
+        constexpr int TB = decltype(tp_c)::value;  // tiles in this batch, all valid
+        int Ia[TB], Ja[TB], da[TB];
+        f32x4 acc[TB];
 #pragma unroll
-      for (int kt0 = 0; kt0 < MAXPT; kt0 += TP) {
-        int Ia[TP], Ja[TP], da[TP];
-        bool ok[TP];
-        f32x4 acc[TP];
-#pragma unroll
-        for (int u = 0; u < TP; ++u) {
+        for (int u = 0; u < TB; ++u) {
           const int t = w + (kt0 + u) * NW;
-          ok[u] = (kt0 + u < MAXPT) && (NPT % NW == 0 || t < NPT);
           int Ip, Jp;
-          tile_of<CT>(ok[u] ? t : 0, Ip, Jp);
+          tile_of<CT>(t, Ip, Jp);
           Ia[u] = rev ? CT - 1 - Ip : Ip;
           Ja[u] = rev ? CT - 1 - Jp : Jp;
           da[u] = Ip - Jp;
@@ -544,9 +545,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         }
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-          bf16x8 A[TP][NT], Bq[TP][NT];
+          bf16x8 A[TB][NT], Bq[TB][NT];
 #pragma unroll
-          for (int u = 0; u < TP; ++u)
+          for (int u = 0; u < TB; ++u)
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
               A[u][p] = lds_read_b128(&sK[p * CP * PK + (16 * Ja[u] + li) * PK + 32 * ks +
@@ -554,10 +555,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
               Bq[u][p] = lds_read_b128(&sQ[p * CP * PQ + (16 * Ia[u] + li) * PQ + 32 * ks + 8 * g]);
             }
 #pragma unroll
-          for (int u = 0; u < TP; ++u) mma_split<NT, NT>(acc[u], A[u], Bq[u]);
+          for (int u = 0; u < TB; ++u) mma_split<NT, NT>(acc[u], A[u], Bq[u]);
         }
 #pragma unroll
-        for (int u = 0; u < TP; ++u) {
+        for (int u = 0; u < TB; ++u) {
           // acc[r] = q'_i . k'_j with i = 16 I + li, j = 16 J + 4 g + r.  The
           // diagonal tile takes the per-lane mask; off the diagonal the
           // exponent is 16 d + base -/+ r (d = Ip - Jp >= 1), formed as
@@ -573,12 +574,23 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[u][r] *= da[u] == 0 ? dmask[r] : s16 * lp[r];
           }
-          if (ok[u]) {
-            if constexpr (ALIAS_P) ptile[(kt0 + u) < MAXPT ? kt0 + u : MAXPT - 1] = acc[u];
-            else put_p(16 * Ia[u] + li, Ja[u], acc[u]);
-          }
+          if constexpr (ALIAS_P) ptile[kt0 + u] = acc[u];
+          else put_p(16 * Ia[u] + li, Ja[u], acc[u]);
         }
         if constexpr (TIGHT) __builtin_amdgcn_sched_barrier(0);
+      };
+      // slot kt is valid iff w + kt NW < NPT; valid slots come first
+      auto slot_ok = [&](int kt) { return kt < MAXPT && (NPT % NW == 0 || w + kt * NW < NPT); };
+#pragma unroll
+      for (int kt0 = 0; kt0 < MAXPT; kt0 += TP) {
+        if constexpr (NPT % NW == 0 && MAXPT % TP == 0) {
+          p_batch(std::integral_constant<int, TP>{}, kt0);  // every slot is a tile
+        } else if constexpr (TP == 2) {
+          if (slot_ok(kt0 + 1)) p_batch(std::integral_constant<int, 2>{}, kt0);
+          else if (slot_ok(kt0)) p_batch(std::integral_constant<int, 1>{}, kt0);
+        } else {
+          if (slot_ok(kt0)) p_batch(std::integral_constant<int, 1>{}, kt0);
+        }
       }
       if constexpr (!ALIAS_P) put_zero_tiles();
     }
