@@ -70,6 +70,30 @@ def event_time_ms(fn, n, stream):
     return s.elapsed_time(e) / n
 
 
+def call_stats(fn, stream, n=20):
+    """Per-call figures after warm-up: the median and minimum of n calls
+    timed one by one with HIP events while the calls run back to back, and
+    the median host wall time of an isolated call (launch, run, synchronize)."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(s.elapsed_time(e) for s, e in ev)
+    lat = []
+    for _ in range(n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t0) * 1e3)
+    lat.sort()
+    return dict(ms_median=per[n // 2], ms_min=per[0], ms_single_call_median=lat[n // 2])
+
+
 def warm_up(fn, min_seconds=0.05):
     """Run fn until min_seconds of wall time have passed.  After the host has
     generated a workload's inputs the GPU has been idle, and its clock takes
@@ -185,7 +209,8 @@ def bench_fwd_only(gla, inputs, name, reps, chunk=C):
     units = B * H * T
     nbytes = units * FWD_BYTES + (2 if S0 is not None else 1) * B * H * STATE_BYTES
     return dict(workload=name, B=B, H=H, T=T, chunk=chunk, ms=ms, tokens_per_s=B * T / (ms / 1e3),
-                gbs=nbytes / (ms / 1e3) / 1e9, hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+                gbs=nbytes / (ms / 1e3) / 1e9, hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                per_call=call_stats(fn, torch.cuda.current_stream()))
 
 
 def bench_decode(gla, inputs, steps_override=None):
@@ -238,6 +263,21 @@ def bench_decode(gla, inputs, steps_override=None):
                                            aug, gam, 1e-6, y=o)
     warm_up(fused)
     fused_ms = event_time_ms(fused, 20, stream)
+    # per-call samples: one step's 24 layer calls, each timed with its own events
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(Lyr)]
+    for layer, (s1, e1) in enumerate(ev):
+        blk = qkv[0, layer]
+        s1.record(stream)
+        gla.decode_step_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, S[layer], o=o)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(s1.elapsed_time(e1) for s1, e1 in ev)
+    # device stream ceiling for the same state traffic: an in-place scale of
+    # one layer's states (read and write every state once, as a decode call does)
+    scale = lambda: S[0].mul_(0.9999)
+    warm_up(scale)
+    ms_scale = event_time_ms(scale, 20, stream)
+    scale_gbs = S[0].numel() * 8 / (ms_scale / 1e3) / 1e9
     return dict(
         workload="decode: 1280 seqs x 24 layers x H=16, fp32 96x192 states, 64 steps, bf16 q/k/v",
         N=N, layers=Lyr, H=H, steps=steps, ms_total=ms, ms_per_layer_call=per_call_ms,
@@ -245,6 +285,9 @@ def bench_decode(gla, inputs, steps_override=None):
         hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         state_gb=S.numel() * 4 / 1e9,
         ms_per_layer_call_fused_epilogue=fused_ms,
+        per_call=dict(ms_median=per[Lyr // 2], ms_min=per[0], calls=Lyr),
+        stream_ceiling=dict(kernel="in-place scale of one layer's states (torch mul_)", gbs=scale_gbs,
+                            decode_frac_of_it=(nbytes / (ms / 1e3) / 1e9) / scale_gbs),
     )
 
 
@@ -422,7 +465,14 @@ def cpu_baseline(inputs, min_seconds=5.0):
         if dt >= min_seconds:
             break
     B, T = x["cfg"]["B"], x["cfg"]["T"]
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return dict(value=reps * B * T / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                cpu_model=cpu_model,
                 sample=f"{reps} fwd+bwd pass(es) of the full training workload (B=8, H=16, "
                        f"T=2048, fp64 oracle), {dt:.2f} s wall")
 
