@@ -52,6 +52,34 @@ def test_conv_optional_operands(gla, bias, state):
     check_conv(gla, c, "bf16", with_state=state)
 
 
+@pytest.mark.parametrize("D,dtype", [(520, "bf16"), (1048, "f32"), (1048, "bf16")])
+def test_conv_partial_channel_block(gla, D, dtype):
+    """Widths that end in a partly filled workgroup after full ones (a
+    workgroup covers 512 channels): its taps are staged by every thread,
+    also those past the last channel, which then leave without output."""
+    flush(f"test_conv_partial_channel_block D={D} {dtype}")
+    c = inputs.conv_inputs(590 + D, 3, 37, D, dtype)
+    check_conv(gla, c, dtype)
+
+
+@pytest.mark.parametrize("D", [520, 1048])
+def test_conv_step_partial_channel_block(gla, D):
+    """The decode step at the same widths, three steps, windows in place."""
+    flush(f"test_conv_step_partial_channel_block D={D}")
+    N, steps = 9, 3
+    c = inputs.conv_inputs(600 + D, N, steps, D, "bf16")
+    w, b = dev_f32(c["w"]), dev_f32(c["bias"])
+    state = dev_f32(c["state"])
+    ref = c["state"].copy()
+    for t in range(steps):
+        x = dev(np.ascontiguousarray(c["x"][:, t]), "bf16")
+        y = gla.conv1d_step_(x, w, b, state, out_dtype=torch.float32)
+        ry, ref = oracle.conv1d_step(c["x"][:, t], c["w"], c["bias"], ref)
+        torch.cuda.synchronize()
+        assert oracle.rel_err(host(y), ry) <= TOL
+    assert np.array_equal(host(state), ref)
+
+
 def test_conv_page_width_bf16(gla):
     """The page's D = 3,072 channels, bf16 activations, fp32 and bf16 outputs."""
     flush("test_conv_page_width_bf16")
