@@ -322,14 +322,46 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   if (bh >= BH) return;
   // the state pass produces what later segments (in walk order) consume
   if (SO && (REV ? seg == 0 : seg == nseg - 1)) return;
-  const int64_t b = bh / a.H;
+  int64_t b = bh / a.H;
   const int64_t h = bh - b * a.H;
+  int64_t bhu = bh;  // the (sequence, head) unit this workgroup serves
+  // Packed sequences of mixed lengths are served longest first: unit index b
+  // takes the sequence of rank b in descending length order (ties by index),
+  // so the long sequences start in the first dispatch wave and the short
+  // ones fill in behind them.  Each workgroup ranks the lengths itself (they
+  // are on the device only), N^2 / threads comparisons from an LDS copy; up
+  // to 512 sequences.  Every unit is still served exactly once.
+  if (a.cu != nullptr && a.B <= 512) {
+    int* const s_pick = reinterpret_cast<int*>(smem);  // query-tile bytes, free until its first store
+    int* const s_len = s_pick + 1;
+    const int nb = (int)a.B;
+    for (int j = threadIdx.x; j < nb; j += NTHR) {
+      int64_t c0 = a.cu[j], c1 = a.cu[j + 1];
+      c0 = c0 < 0 ? 0 : (c0 > a.T ? a.T : c0);
+      c1 = c1 < c0 ? c0 : (c1 > a.T ? a.T : c1);
+      s_len[j] = (int)(c1 - c0);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nb; j += NTHR) {
+      const int lj = s_len[j];
+      int rank = 0;
+      for (int i = 0; i < nb; ++i) {
+        const int li2 = s_len[i];
+        rank += (li2 > lj || (li2 == lj && i < j)) ? 1 : 0;
+      }
+      if (rank == (int)b) s_pick[0] = j;
+    }
+    __syncthreads();
+    b = s_pick[0];
+    bhu = b * a.H + h;
+    __syncthreads();  // every thread has read the pick before the tile stores reuse these bytes
+  }
 
   // this unit's tokens and state: the dense (b, h) layout, or a packed
   // sequence with its state in a pool page
   int64_t T = a.T, tbase = 0;
-  const float* s_init = a.s_init ? a.s_init + bh * (int64_t)DK * DV : nullptr;
-  float* s_final = a.s_final ? a.s_final + bh * (int64_t)DK * DV : nullptr;
+  const float* s_init = a.s_init ? a.s_init + bhu * (int64_t)DK * DV : nullptr;
+  float* s_final = a.s_final ? a.s_final + bhu * (int64_t)DK * DV : nullptr;
   if (a.cu) {
     int64_t c0 = a.cu[b], c1 = a.cu[b + 1];
     c0 = c0 < 0 ? 0 : (c0 > a.T ? a.T : c0);
