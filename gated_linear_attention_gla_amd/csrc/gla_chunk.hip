@@ -254,7 +254,7 @@ struct ChunkLds {
 // kernels below).  SO (state only): the segment state pass -- only the state
 // update runs, from a zero state, and the segment's end state goes to
 // a.seg_state.
-template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false>
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false, bool PACKED = false>
 __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, char* const smem) {
   using Lds = ChunkLds<DK, BN, C, NT, NW, EPI>;
   constexpr int NTHR = NW * 64;
@@ -330,8 +330,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // so the long sequences start in the first dispatch wave and the short
   // ones fill in behind them.  Each workgroup ranks the lengths itself (they
   // are on the device only), N^2 / threads comparisons from an LDS copy; up
-  // to 512 sequences.  Every unit is still served exactly once.
-  if (a.cu != nullptr && a.B <= 512) {
+  // to 512 sequences.  Every unit is still served exactly once.  (A separate
+  // instantiation, so the dense kernels' code is untouched.)
+  if constexpr (PACKED) {
+    if (a.B <= 512) {
     int* const s_pick = reinterpret_cast<int*>(smem);  // query-tile bytes, free until its first store
     int* const s_len = s_pick + 1;
     const int nb = (int)a.B;
@@ -355,6 +357,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     b = s_pick[0];
     bhu = b * a.H + h;
     __syncthreads();  // every thread has read the pick before the tile stores reuse these bytes
+    }
   }
 
   // this unit's tokens and state: the dense (b, h) layout, or a packed
@@ -1052,10 +1055,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   }
 }
 
-template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false>
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false, bool PACKED = false>
 __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW, EPI>::BYTES];
-  chunk_body<DK, DV, BN, NW, C, NT, REV, SO, EPI>(a, blockIdx.x, smem);
+  chunk_body<DK, DV, BN, NW, C, NT, REV, SO, EPI, PACKED>(a, blockIdx.x, smem);
 }
 
 // Two independent passes of one shape in one launch, the first in forward
@@ -1084,6 +1087,8 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (a.reverse) hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, true, false>), grid, block, 0, st, a);
+  else if (a.cu != nullptr && a.nseg == 1)  // packed sequences (forward, no segments)
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false, false, false, true>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
