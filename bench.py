@@ -565,6 +565,9 @@ def main():
         log(f"bench: {name} fwd")
         extra[name + "_fwd"] = bench_fwd_only(gla, inputs, name, reps)
         log(f"  {extra[name + '_fwd']['ms']:.3f} ms")
+        # the same workload at the pages' 128-token chunk (results agree up to rounding)
+        extra[name + f"_fwd_chunk{C_PAGE}"] = bench_fwd_only(gla, inputs, name, reps, chunk=C_PAGE)
+        log(f"  chunk {C_PAGE}: {extra[name + f'_fwd_chunk{C_PAGE}']['ms']:.3f} ms")
     log(f"bench: training shape fwd+bwd at the pages' {C_PAGE}-token chunk")
     extra["training_chunk128"] = bench_fwd_bwd_events(gla, inputs, "training", 20, chunk=C_PAGE)
     log(f"  fwd {extra['training_chunk128']['ms_fwd']:.3f} ms  bwd {extra['training_chunk128']['ms_bwd']:.3f} ms")
