@@ -89,6 +89,20 @@ def test_varlen_serving_mix(gla):
         assert oracle.rel_err(pool[sl, 0][None], rS) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("n,chunk", [(300, 16), (600, 32)])
+def test_varlen_many_sequences_with_ties(gla, n, chunk):
+    """Many short sequences with heavily repeated lengths (ties in the
+    longest-first order are broken by index), below and above the 512
+    sequences up to which the workgroups rank the lengths (natural order
+    beyond): every sequence must be served exactly once."""
+    flush(f"test_varlen_many_sequences_with_ties n={n} chunk={chunk}")
+    rng = np.random.default_rng(650 + n)
+    lengths = rng.choice([0, 1, 5, 16, 17, 33], size=n)
+    x = inputs.varlen_inputs(650 + n, lengths, 2, 16, 32, num_slots=n + 7, dtype="f32")
+    x["lam"] = inputs.round_f32(np.array([0.7, 0.99]))
+    check_varlen(gla, x, "f32", chunk)
+
+
 def test_varlen_identity_slots_all_continue(gla):
     """slots = NULL (sequence n uses page n) and has_state = NULL (all continue)."""
     flush("test_varlen_identity_slots_all_continue")
