@@ -113,6 +113,32 @@ def test_fwd_laplace_full(gla, chunk):
     assert np.max(np.abs(a - b)) <= 1
 
 
+
+def test_fwd_long_context_full(gla):
+    """Long-context prefill at its full size (B=1, H=16, T=65,536, bf16,
+    lambda in [0.95, 0.9999]) in the launch configurations the benchmark times
+    (64- and 128-token chunks, 8 segments per head): the whole fp32-stored
+    output and the final state against the oracle, and the bf16-stored output
+    equal to the fp32-stored one rounded to nearest, within one bf16 ulp."""
+    flush("test_fwd_long_context_full T=65536")
+    x = inputs.make_chunk_inputs("long")
+    ro, rS = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    q, k, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+    lam, S0 = dev_f32(x["lam"]), dev_f32(x["S0"])
+    for chunk in (64, 128):
+        assert segments_of(gla, 1, 16, 65536, 96, 192, chunk) >= 2
+        o32, S32 = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.float32)
+        o16, _ = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        eo, eS = oracle.rel_err(host(o32), ro), oracle.rel_err(host(S32), rS)
+        flush(f"  chunk={chunk} err o={eo:.3e} S_T={eS:.3e}")
+        assert eo <= TOL["bf16"] and eS <= TOL["bf16"]
+        a = o16.view(torch.int16).cpu().numpy().astype(np.int32)
+        b = o32.to(torch.bfloat16).view(torch.int16).cpu().numpy().astype(np.int32)
+        assert np.max(np.abs(a - b)) <= 1
+        del o32, o16, S32
+
+
 def test_fwd_token_major_layout(gla):
     """q, k, v, o as (B, T, H, d) storage viewed as (B, H, T, d)."""
     flush("test_fwd_token_major_layout")
