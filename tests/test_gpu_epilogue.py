@@ -122,3 +122,58 @@ def test_fused_decode_steps(gla, dims):
         torch.cuda.synchronize()
         assert oracle.rel_err(host(y), ry) <= 1e-5
     assert oracle.rel_err(host(S), Sref) <= 1e-5
+
+
+def test_fused_decode_full_slab_sampled(gla):
+    """The fused decode step in the launch configuration the benchmark times:
+    one 1,280 x 16 slab of fp32 96 x 192 states, q/k/v as strided views of one
+    packed bf16 block per step, a bf16 gate stream, bf16 output.  Two steps.
+    Each call is repeated with fp32 output on a copy of the slab and with the
+    plain decode step on another copy: the three state updates must agree bit
+    for bit, the bf16 output must be the fp32 output rounded to nearest
+    (within one bf16 ulp), and for 12 sampled (sequence, head) pairs the fp32
+    output and the state must match oracle.decode_step + oracle.epilogue to
+    1e-5."""
+    flush("test_fused_decode_full_slab_sampled N=1280 H=16")
+    N, H, dk, dv, steps = 1280, 16, 96, 192, 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5_000_303)
+    S = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+    S.normal_(0.0, 0.01, generator=g)
+    qkv = torch.randn((steps, N, H, dk + dk + dv), generator=g, device="cuda").to(torch.bfloat16)
+    gz = torch.randn((steps, N, H, dv), generator=g, device="cuda").to(torch.bfloat16)
+    aug = (0.2 * torch.randn((H, dk), generator=g, device="cuda")).contiguous()
+    gam = (1.0 + 0.1 * torch.randn((H, dv), generator=g, device="cuda")).contiguous()
+    lam_h = np.asarray(inputs.lambda_log_spaced(H, 0.95, 0.9999), dtype=np.float32)
+    lam = dev_f32(lam_h)
+    aug_h, gam_h = host(aug), host(gam)
+    rng = np.random.default_rng(11)
+    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, N, 12), rng.integers(0, H, 12))]
+    ref_S = {(n, h): host(S[n, h]) for n, h in pairs}
+    y16 = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
+    for st in range(steps):
+        blk, gs = qkv[st], gz[st]
+        qv, kv, vv = blk[..., :dk], blk[..., dk:2 * dk], blk[..., 2 * dk:]
+        S32, Spl = S.clone(), S.clone()
+        gla.decode_step_fused_(qv, kv, vv, lam, S, gs, aug, gam, EPS, y=y16)
+        y32 = gla.decode_step_fused_(qv, kv, vv, lam, S32, gs, aug, gam, EPS, out_dtype=torch.float32)
+        gla.decode_step_(qv, kv, vv, lam, Spl, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(S, S32) and torch.equal(S, Spl), st
+        del S32, Spl
+        a = y16.view(torch.int16).cpu().numpy().astype(np.int32)
+        b = y32.to(torch.bfloat16).view(torch.int16).cpu().numpy().astype(np.int32)
+        assert np.max(np.abs(a - b)) <= 1, st
+        got, bh, gh = host(y32), host(blk), host(gs)
+        for n, h in pairs:
+            q1 = bh[n, h, :dk][None, None, None]
+            k1 = bh[n, h, dk:2 * dk][None, None, None]
+            v1 = bh[n, h, 2 * dk:][None, None, None]
+            ro, rS = oracle.decode_step(q1[:, :, 0], k1[:, :, 0], v1[:, :, 0], lam_h[h:h + 1],
+                                        ref_S[(n, h)][None, None])
+            ref_S[(n, h)] = rS[0, 0]
+            ry = oracle.epilogue(q1, k1, v1, ro[:, :, None], aug_h[h:h + 1], gam_h[h:h + 1], EPS,
+                                 gh[n, h][None, None, None])
+            assert oracle.rel_err(got[n, h], ry[0, 0, 0]) <= 1e-5, (st, n, h)
+    for n, h in pairs:
+        assert oracle.rel_err(host(S[n, h]), ref_S[(n, h)]) <= 1e-5, (n, h)
