@@ -151,6 +151,34 @@ def test_conv_decode_steps(gla, dtype):
     assert np.array_equal(host(state), ref)
 
 
+
+def test_conv_decode_step_full_batch(gla):
+    """The decode step in the launch configuration the benchmark times:
+    1,280 sequences x D = 3,072, bf16 input, fp32 windows, bias, two steps.
+    The fp32-stored output and the windows against the oracle; the
+    bf16-stored output of the same step (on a copy of the windows) equal to
+    the fp32-stored one rounded to nearest, within one bf16 ulp."""
+    flush("test_conv_decode_step_full_batch N=1280 D=3072")
+    N, D, steps = 1280, 3072, 2
+    c = inputs.conv_inputs(575, N, steps, D, "bf16")
+    w, b = dev_f32(c["w"]), dev_f32(c["bias"])
+    state = dev_f32(c["state"])
+    ref = c["state"].copy()
+    y16 = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
+    for t in range(steps):
+        x = dev(np.ascontiguousarray(c["x"][:, t]), "bf16")
+        st16 = state.clone()
+        gla.conv1d_step_(x, w, b, st16, y=y16)
+        y = gla.conv1d_step_(x, w, b, state, out_dtype=torch.float32)
+        ry, ref = oracle.conv1d_step(c["x"][:, t], c["w"], c["bias"], ref)
+        torch.cuda.synchronize()
+        assert oracle.rel_err(host(y), ry) <= TOL, t
+        assert torch.equal(st16, state), t
+        a = y16.view(torch.int16).cpu().numpy().astype(np.int32)
+        bb = y.to(torch.bfloat16).view(torch.int16).cpu().numpy().astype(np.int32)
+        assert np.max(np.abs(a - bb)) <= 1, t
+    assert np.array_equal(host(state), ref)
+
 def test_conv_decode_page_pool(gla):
     """Windows inside a per-sequence page holding several layers: only the
     addressed layer's window changes."""
