@@ -221,11 +221,28 @@ def test_bwd_bf16_ragged(gla, chunk):
 
 @pytest.mark.parametrize("chunk", [64, 128])
 def test_bwd_training_full_sampled(gla, chunk):
-    """Full training shape (B=8, H=16, T=2048) in the benched launch (chunk
-    64; 128 as well); the oracle recomputes the (b, h) units of b in {0, 7}
-    (units are independent)."""
+    """Full training shape (B=8, H=16, T=2048) in the benched launches (chunk
+    64; 128 as well), forward and backward; the oracle recomputes the (b, h)
+    units of b in {0, 7} (units are independent).  The forward's bf16-stored
+    output must be its fp32-stored output rounded to nearest, within one bf16
+    ulp, over the whole batch."""
     flush(f"test_bwd_training_full_sampled chunk={chunk}")
     x = inputs.make_chunk_inputs("training", with_grad=True)
+    q, k, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+    lam, S0 = dev_f32(x["lam"]), dev_f32(x["S0"])
+    o32, S32 = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.float32)
+    o16, _ = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    a = o16.view(torch.int16).cpu().numpy().astype(np.int32)
+    bb = o32.to(torch.bfloat16).view(torch.int16).cpu().numpy().astype(np.int32)
+    assert np.max(np.abs(a - bb)) <= 1
+    for b in (0, 7):
+        sl = slice(b, b + 1)
+        ro, rS = oracle.fwd(x["q"][sl], x["k"][sl], x["v"][sl], x["lam"], x["S0"][sl])
+        eo, eS = oracle.rel_err(host(o32[sl]), ro), oracle.rel_err(host(S32[sl]), rS)
+        flush(f"  b={b} fwd err o={eo:.3e} S_T={eS:.3e}")
+        assert eo <= TOL["bf16"] and eS <= TOL["bf16"]
+    del q, k, v, o32, o16, S32
     g = run_bwd(gla, x, "bf16", chunk)
     for b in (0, 7):
         sl = slice(b, b + 1)
