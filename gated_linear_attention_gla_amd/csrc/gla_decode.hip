@@ -8,29 +8,35 @@
 //
 // Per (n, h):  S <- lam S + k v^T  (in place),  o = S^T q  (updated state).
 // The step is a pure HBM stream (each state is read once and written once),
-// so there is no MFMA: one workgroup owns one state; thread (cg, rp) owns the
-// four columns 4 cg..4 cg+3 and the rows rp, rp + RP, ...  A wavefront's
-// 16-byte accesses cover whole state rows, fully coalesced.  Column partial
-// sums of o are combined across the RP row phases through LDS.
+// so there is no MFMA.  A workgroup owns every row of CB-th of the state's
+// columns (CB = 1: the whole state); thread (cg, rp) owns the four columns
+// 4 cg..4 cg+3 of that slice and the rows rp, rp + RP, ...  Each row segment
+// is read with whole 16-byte vectors, and the readout's column sums stay in
+// the workgroup: the RP row-phase partials are combined through LDS.
 #include "gla_common.hpp"
 #include "gla_internal.h"
 
 namespace gla {
 
-template <int DK, int DV, int RP, bool EPI = false>
-__global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
-  constexpr int CG = DV / 4;          // float4 column groups
+template <int DK, int DV, int RP, bool EPI = false, int CB = 1>
+__global__ void __launch_bounds__((DV / 4 / CB) * RP) decode_kernel(DecodeArgs a) {
+  constexpr int CGS = DV / 4;         // float4 column groups of a state row
+  constexpr int CG = CGS / CB;        // ... of this workgroup's column slice
+  static_assert(CGS % CB == 0, "column slices of whole float4 groups");
+  static_assert(!EPI || CB == 1, "the epilogue normalises whole rows");
   constexpr int NTHR = CG * RP;
+  static_assert(NTHR >= DK, "one thread per q, k element");
   constexpr int RPT = (DK + RP - 1) / RP;  // rows per thread
   __shared__ float sq[DK];
   __shared__ float sk[DK];
   __shared__ float4 so[RP][CG];
 
-  const int64_t nh = blockIdx.x;
+  const int64_t nh = blockIdx.x / CB;
   const int64_t n = nh / a.H;
   const int64_t h = nh - n * a.H;
   const int tid = threadIdx.x;
-  const int cg = tid % CG;
+  const int cs = (int)(blockIdx.x % CB) * CG;  // first column group of the slice
+  const int cg = cs + tid % CG;
   const int rp = tid / CG;
 
   if (tid < DK) {
@@ -62,7 +68,7 @@ __global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int d = rp + i * RP;
-    if (d < DK) st[i] = __builtin_nontemporal_load(&S[d * CG + cg]);
+    if (d < DK) st[i] = __builtin_nontemporal_load(&S[d * CGS + cg]);
   }
   __syncthreads();  // sq, sk ready
 
@@ -77,7 +83,7 @@ __global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
       s[1] = fmaf(lam, s[1], kd * vv.y);
       s[2] = fmaf(lam, s[2], kd * vv.z);
       s[3] = fmaf(lam, s[3], kd * vv.w);
-      __builtin_nontemporal_store(s, &S[d * CG + cg]);
+      __builtin_nontemporal_store(s, &S[d * CGS + cg]);
       acc.x = fmaf(qd, s[0], acc.x);
       acc.y = fmaf(qd, s[1], acc.y);
       acc.z = fmaf(qd, s[2], acc.z);
@@ -95,7 +101,7 @@ __global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
       if (tid == 0) sgate = 1.0f / (1.0f + expf(-part));
     }
   }
-  so[rp][cg] = acc;
+  so[rp][cg - cs] = acc;
   __syncthreads();
   static_assert(CG <= 64, "the first wave finishes the output");
   if (tid < 64) {
@@ -140,7 +146,7 @@ __global__ void __launch_bounds__((DV / 4) * RP) decode_kernel(DecodeArgs a) {
       }
     }
     if (own) {
-      const int64_t oo = n * a.so_n + h * a.so_h + 4 * tid;
+      const int64_t oo = n * a.so_n + h * a.so_h + 4 * (cs + tid);
       if (a.o_f32) {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + oo) = r;
       } else {
@@ -164,7 +170,14 @@ hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st) {
   if (nblocks <= 0) return hipSuccess;
   const bool epi = a.gz != nullptr;
   if (dk == 96 && dv == 192) {
+    // The plain step streams three 64-column slices per state (16 column
+    // groups x 24 row phases, 4 rows per thread), which measured faster than
+    // a workgroup per state and than 12 or 48 row phases.  The grid's
+    // work-item count must fit 32 bits: up to 2^22 states (more than 288 GB of
+    // them) it does; beyond, one workgroup per state.
     if (epi) hipLaunchKernelGGL((decode_kernel<96, 192, 4, true>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
+    else if (nblocks <= (int64_t{1} << 22))
+      hipLaunchKernelGGL((decode_kernel<96, 192, 24, false, 3>), dim3((unsigned)(nblocks * 3)), dim3(16 * 24), 0, st, a);
     else hipLaunchKernelGGL((decode_kernel<96, 192, 4>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
   } else if (dk == 16 && dv == 32) {
     if (epi) hipLaunchKernelGGL((decode_kernel<16, 32, 8, true>), dim3((unsigned)nblocks), dim3(8 * 8), 0, st, a);
