@@ -137,6 +137,9 @@ def bench_train(gla, inputs, steps, warmup, chunk=C):
         fwd()
         bwd()
 
+    # the GPU clock first has to come back to speed after input generation
+    # (warm_up), then the requested number of untimed steps
+    warm_up(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -185,8 +188,12 @@ def bench_fwd_bwd_events(gla, inputs, name, reps, chunk=C):
     stream = torch.cuda.current_stream()
     ms_fwd = event_time_ms(fwd, reps, stream)
     ms_bwd = event_time_ms(bwd, reps, stream)
+    units = B * H * T
     return dict(workload=name, B=B, H=H, T=T, chunk=chunk, ms_fwd=ms_fwd, ms_bwd=ms_bwd,
                 tokens_per_s=B * T / ((ms_fwd + ms_bwd) / 1e3),
+                fwd_bytes=units * FWD_BYTES + 2 * B * H * STATE_BYTES,
+                bwd_bytes=units * BWD_BYTES + 2 * B * H * STATE_BYTES,
+                fwd_flops=units * FWD_FLOPS(chunk), bwd_flops=units * BWD_FLOPS(chunk),
                 lam=[float(t) for t in x["lam"]])
 
 
@@ -532,6 +539,33 @@ def oracle_rows(inputs, min_seconds=0.5):
     return out
 
 
+def rooflines(tr, ms_step):
+    """Roofline of the dominant launch (the longer of the forward launch and
+    the backward call: algorithmic bytes per launch over its event-timed
+    duration) and the whole step's HBM, MFMA and attainable fractions."""
+    fwd_gbs = tr["fwd_bytes"] / (tr["ms_fwd"] / 1e3) / 1e9
+    bwd_gbs = tr["bwd_bytes"] / (tr["ms_bwd"] / 1e3) / 1e9
+    if tr["ms_bwd"] >= tr["ms_fwd"]:
+        kernel, achieved, nbytes, ms = "gla_chunk_bwd", bwd_gbs, tr["bwd_bytes"], tr["ms_bwd"]
+    else:
+        kernel, achieved, nbytes, ms = "gla_chunk_fwd", fwd_gbs, tr["fwd_bytes"], tr["ms_fwd"]
+    rf = {"bound": "hbm", "kernel": f"{kernel} (chunk {tr['chunk']})", "achieved": achieved,
+          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+          "bytes_per_launch": nbytes, "ms_per_launch": ms}
+    step_bytes = tr["fwd_bytes"] + tr["bwd_bytes"]
+    step_flops = tr["fwd_flops"] + tr["bwd_flops"]
+    srf = {
+        "algorithmic_bytes": step_bytes,
+        "algorithmic_flops": step_flops,
+        "hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "mfma_frac": step_flops / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+        "attainable_frac": max(step_bytes / (HBM_PEAK_GBS * 1e9),
+                               step_flops / (BF16_PEAK_TFLOPS * 1e12)) / (ms_step / 1e3),
+        "fwd_gbs": fwd_gbs, "bwd_gbs": bwd_gbs, "ms_fwd": tr["ms_fwd"], "ms_bwd": tr["ms_bwd"],
+    }
+    return rf, srf
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -605,17 +639,15 @@ def main():
             if target is not None:
                 target["cpu_oracle"] = rows[key]
 
-    # dominant kernel: the longer of the forward launch and the backward call
-    fwd_gbs = tr["fwd_bytes"] / (tr["ms_fwd"] / 1e3) / 1e9
-    bwd_gbs = tr["bwd_bytes"] / (tr["ms_bwd"] / 1e3) / 1e9
-    if tr["ms_bwd"] >= tr["ms_fwd"]:
-        dom = dict(kernel="gla_chunk_bwd (dq, dv, dk passes)", achieved=bwd_gbs,
-                   bytes_per_launch=tr["bwd_bytes"], ms_per_launch=tr["ms_bwd"])
-    else:
-        dom = dict(kernel="gla_chunk_fwd", achieved=fwd_gbs, bytes_per_launch=tr["fwd_bytes"],
-                   ms_per_launch=tr["ms_fwd"])
-    step_bytes = tr["fwd_bytes"] + tr["bwd_bytes"]
-    step_flops = tr["fwd_flops"] + tr["bwd_flops"]
+    rf, srf = rooflines(tr, tr["ms_step"])
+    rf["traffic"] = counted_traffic() if rf["kernel"].startswith("gla_chunk_bwd") else None
+    srf["mfma_counted"] = counted_mfma()
+    # the same step at the pages' 128-token chunk (config as the pages run it):
+    # its per-launch rooflines, with the step taken as forward + backward
+    t128 = extra["training_chunk128"]
+    rf128, srf128 = rooflines(t128, t128["ms_fwd"] + t128["ms_bwd"])
+    t128["roofline"] = rf128
+    t128["step_roofline"] = srf128
     out = {
         "metric": METRIC,
         "value": tr["tokens_per_s"],
@@ -637,28 +669,8 @@ def main():
             "global_batch": tr["B"], "seq_len": tr["T"], "heads": tr["H"], "dk": DK, "dv": DV,
             "chunk": C, "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": dom["kernel"],
-            "achieved": dom["achieved"],
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": dom["achieved"] / HBM_PEAK_GBS,
-            "traffic": counted_traffic() if dom["kernel"].startswith("gla_chunk_bwd") else None,
-            "bytes_per_launch": dom["bytes_per_launch"],
-            "ms_per_launch": dom["ms_per_launch"],
-        },
-        "step_roofline": {
-            "algorithmic_bytes": step_bytes,
-            "algorithmic_flops": step_flops,
-            "hbm_frac": step_bytes / (tr["ms_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_frac": step_flops / (tr["ms_step"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
-            "attainable_frac": max(step_bytes / (HBM_PEAK_GBS * 1e9),
-                                   step_flops / (BF16_PEAK_TFLOPS * 1e12)) / (tr["ms_step"] / 1e3),
-            "mfma_counted": counted_mfma(),
-            "fwd_gbs": fwd_gbs, "bwd_gbs": bwd_gbs,
-            "ms_fwd": tr["ms_fwd"], "ms_bwd": tr["ms_bwd"],
-        },
+        "roofline": rf,
+        "step_roofline": srf,
         "cpu_baseline": cpu,
         "decode": dec,
         "extra": extra,

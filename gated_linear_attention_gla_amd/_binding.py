@@ -97,6 +97,8 @@ def load_library(path=LIB_PATH):
         P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
         P(GlaTensor), vp,
     ]
+    lib.gla_decode_workgroups_per_state.restype = ctypes.c_int
+    lib.gla_decode_workgroups_per_state.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
     lib.gla_decode_step_fused.restype = ctypes.c_int
     lib.gla_decode_step_fused.argtypes = [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,

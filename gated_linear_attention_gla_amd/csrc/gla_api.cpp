@@ -237,8 +237,9 @@ static gla_status decode_impl(int64_t N, int64_t H, int64_t dk, int64_t dv, cons
                               int64_t S_stride_n, const gla_tensor* g, const float* aug, const float* gamma,
                               float eps, gla_tensor* o, void* stream) {
   if (!q || !k || !v || !lambda || !S || !o) return GLA_ERR_NULL;
-  // one workgroup of dv / 4 * 4 threads per (n, h): N * H <= 2^24 keeps the
-  // launch below 2^32 work-items
+  // N * H <= 2^24 states: the launch (gla::decode_slices picks three column
+  // slices per state while they fit, else one 192-thread workgroup per
+  // state) then stays below 2^32 work-items
   if (N < 1 || H < 1 || dk < 1 || dv < 1 || N > (int64_t)1 << 30 || H > (int64_t)1 << 16 ||
       N * H > (int64_t)1 << 24)
     return GLA_ERR_SHAPE;
@@ -298,6 +299,12 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
                            const gla_tensor* k, const gla_tensor* v, const float* lambda,
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream) {
   return decode_impl(N, H, dk, dv, q, k, v, lambda, S, S_stride_n, nullptr, nullptr, nullptr, 0.0f, o, stream);
+}
+
+int gla_decode_workgroups_per_state(int64_t N, int64_t H, int64_t dk, int64_t dv, int fused) {
+  if (N < 1 || H < 1 || N > (int64_t)1 << 30 || H > (int64_t)1 << 16 || N * H > (int64_t)1 << 24) return 0;
+  if (dk < 1 || dv < 1 || dk > 4096 || dv > 4096) return 0;
+  return gla::decode_slices(N * H, (int)dk, (int)dv, fused != 0);
 }
 
 gla_status gla_decode_step_fused(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,

@@ -165,25 +165,44 @@ bool decode_supported(int dk, int dv) {
   return (dk == 96 && dv == 192) || (dk == 16 && dv == 32);
 }
 
+// Threads of one decode workgroup, and how many column slices (workgroups)
+// serve each state.  The (96, 192) plain step streams three 64-column slices
+// per state (16 column groups x 24 row phases, 4 rows per thread), which
+// measured faster than a workgroup per state and than 12 or 48 row phases;
+// the fused step normalises whole rows, so it keeps one workgroup per state.
+// A launch covers at most 2^32 - 1 work-items: with 384 threads per slice,
+// three slices fit up to 3,728,270 states (about 275 GB of fp32 states);
+// beyond that the step falls back to one 192-thread workgroup per state.
+static int decode_threads(int dk, int dv, bool epi, int slices) {
+  if (dk == 96 && dv == 192) return slices == 3 ? 16 * 24 : 48 * 4;
+  (void)epi;
+  return 8 * 8;
+}
+
+int decode_slices(int64_t states, int dk, int dv, bool epi) {
+  if (!decode_supported(dk, dv) || states < 1) return 0;
+  if (dk == 96 && dv == 192 && !epi) {
+    const int64_t items = states * 3 * decode_threads(dk, dv, epi, 3);
+    if (items <= (int64_t)0xFFFFFFFF) return 3;
+  }
+  return 1;
+}
+
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st) {
   const int64_t nblocks = a.N * a.H;
   if (nblocks <= 0) return hipSuccess;
   const bool epi = a.gz != nullptr;
-  if (dk == 96 && dv == 192) {
-    // The plain step streams three 64-column slices per state (16 column
-    // groups x 24 row phases, 4 rows per thread), which measured faster than
-    // a workgroup per state and than 12 or 48 row phases.  The grid's
-    // work-item count must fit 32 bits: up to 2^22 states (more than 288 GB of
-    // them) it does; beyond, one workgroup per state.
-    if (epi) hipLaunchKernelGGL((decode_kernel<96, 192, 4, true>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
-    else if (nblocks <= (int64_t{1} << 22))
-      hipLaunchKernelGGL((decode_kernel<96, 192, 24, false, 3>), dim3((unsigned)(nblocks * 3)), dim3(16 * 24), 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<96, 192, 4>), dim3((unsigned)nblocks), dim3(48 * 4), 0, st, a);
-  } else if (dk == 16 && dv == 32) {
-    if (epi) hipLaunchKernelGGL((decode_kernel<16, 32, 8, true>), dim3((unsigned)nblocks), dim3(8 * 8), 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<16, 32, 8>), dim3((unsigned)nblocks), dim3(8 * 8), 0, st, a);
-  } else {
+  const int slices = decode_slices(nblocks, dk, dv, epi);
+  if (slices == 0 || nblocks * slices * decode_threads(dk, dv, epi, slices) > (int64_t)0xFFFFFFFF)
     return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(nblocks * slices)), block(decode_threads(dk, dv, epi, slices));
+  if (dk == 96 && dv == 192) {
+    if (epi) hipLaunchKernelGGL((decode_kernel<96, 192, 4, true>), grid, block, 0, st, a);
+    else if (slices == 3) hipLaunchKernelGGL((decode_kernel<96, 192, 24, false, 3>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<96, 192, 4>), grid, block, 0, st, a);
+  } else {
+    if (epi) hipLaunchKernelGGL((decode_kernel<16, 32, 8, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<16, 32, 8>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -131,6 +131,10 @@ int chunk_segments_fused(int64_t B, int64_t H, int64_t T, int chunk);
 hipError_t launch_chunk_fused(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st);
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
 bool decode_supported(int dk, int dv);
+// Workgroups (column slices) the decode step launches per state for `states`
+// states (0 when the shape has no kernel); the launch stays below 2^32
+// work-items for every state count the ABI accepts.
+int decode_slices(int64_t states, int dk, int dv, bool epi);
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);
 hipError_t launch_conv_step(const ConvStepArgs& a, hipStream_t st);
 // one-dimensional grid sizes of the two convolution launches, and their

@@ -155,6 +155,15 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
                            const gla_tensor* k, const gla_tensor* v, const float* lambda,
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream);
 
+/* Launch shape of the decode step, for capacity planning and tests (calling
+ * it is never required): the number of workgroups gla_decode_step (fused = 0)
+ * or gla_decode_step_fused (fused != 0) launches per (n, h) state for these
+ * sizes, or 0 when that call would reject them.  The (96, 192) plain step
+ * splits each state into 3 column slices while N * H * 3 * 384 work-items
+ * fit one launch (up to 3,728,270 states), else it runs one workgroup per
+ * state; the fused step always runs one workgroup per state. */
+int gla_decode_workgroups_per_state(int64_t N, int64_t H, int64_t dk, int64_t dv, int fused);
+
 /* Chunked forward with the mixer's output epilogue fused into the store
  * (page section "GLA mixer", after the readout: self-augmentation adds a
  * gated copy of the value, the gate being the sigmoid of the query-key dot

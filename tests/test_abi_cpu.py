@@ -235,6 +235,26 @@ def test_decode_validation(lib):
     assert dec(lib, 4, 2, 96, 192, q, k, v, S=k.data, o=o) == ALIAS
 
 
+def test_decode_launch_shape_boundary(lib):
+    """The decode step's per-state workgroup count: three 384-thread column
+    slices while N * H * 1152 work-items fit one launch (2^32 - 1), else one
+    workgroup per state; the fused step always one; 0 for rejected sizes."""
+    f = lib.gla_decode_workgroups_per_state
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+    assert f(1280, 16, 96, 192, 0) == 3
+    assert 3_728_270 * 3 * 384 <= 0xFFFFFFFF < 3_728_271 * 3 * 384
+    assert f(3_728_270, 1, 96, 192, 0) == 3
+    assert f(3_728_271, 1, 96, 192, 0) == 1
+    assert f(1 << 20, 4, 96, 192, 0) == 1  # 2^22 states: the old guard's bound, now one workgroup each
+    assert f(1 << 24, 1, 96, 192, 0) == 1  # the largest N * H gla_decode_step accepts
+    assert f((1 << 24) + 1, 1, 96, 192, 0) == 0
+    assert f(1280, 16, 96, 192, 1) == 1
+    assert f(4, 2, 16, 32, 0) == 1
+    assert f(4, 2, 64, 192, 0) == 0
+    assert f(0, 2, 96, 192, 0) == 0
+
+
 # ------------------------------------------------------------ convolution
 def conv_fwd(lib, B, T, D, x, y, w=0xA000, bias=None, sin=None, sout=None):
     ref = lambda t: None if t is None else ctypes.byref(t)
