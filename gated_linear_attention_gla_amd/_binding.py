@@ -85,6 +85,10 @@ def load_library(path=LIB_PATH):
         P(GlaDims), P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp,
         P(GlaTensor), vp, vp, ctypes.c_size_t, vp,
     ]
+    lib.gla_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gla_chunk_fwd_noalloc.argtypes = [
+        P(GlaDims), P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, P(GlaTensor), vp, vp,
+    ]
     lib.gla_chunk_bwd.restype = ctypes.c_int
     lib.gla_chunk_bwd.argtypes = [
         P(GlaDims), P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp,
@@ -230,6 +234,30 @@ def chunk_fwd(q, k, v, lam, S0=None, chunk=64, out_dtype=None, o=None, S_T=None,
     st = lib.gla_chunk_fwd(
         ctypes.byref(dims), ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
         _ptr(lam), _ptr(S0), ctypes.byref(to), _ptr(S_T), _ptr(ws), nws, _stream(),
+    )
+    _check(lib, st)
+    return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, lam, S0, o, S_T=None, chunk=64):
+    """chunk_fwd into caller-provided o (and S_T) through gla_chunk_fwd_noalloc:
+    the library call allocates nothing (segment states go to the library's
+    static device scratch); returns (o, S_T)."""
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _expect(k, (B, H, T, dk), "k")
+    _expect(v, (B, H, T, dv), "v")
+    _expect(lam, (H,), "lam", torch.float32, contiguous=True)
+    _expect(o, (B, H, T, dv), "o")
+    _state_ok(S0, B, H, dk, dv, "S0")
+    _state_ok(S_T, B, H, dk, dv, "S_T")
+    _same_device(q, k, v, lam, o, S0, S_T)
+    dims = GlaDims(B, H, T, dk, dv, chunk)
+    tq, tk, tv, to = _view4(q), _view4(k), _view4(v), _view4(o)
+    st = lib.gla_chunk_fwd_noalloc(
+        ctypes.byref(dims), ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+        _ptr(lam), _ptr(S0), ctypes.byref(to), _ptr(S_T), _stream(),
     )
     _check(lib, st)
     return o, S_T

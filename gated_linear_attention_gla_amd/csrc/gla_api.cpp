@@ -27,6 +27,16 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
+// Device scratch of gla_chunk_fwd_noalloc: the segment end states of its
+// segment split (the same use as gla_chunk_fwd's workspace).  Every GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device
+// address comes from hipGetSymbolAddress (noalloc_scratch below) and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[GLA_NOALLOC_SCRATCH_BYTES];
+
 using gla::ChunkArgs;
 using gla::DecodeArgs;
 
@@ -113,6 +123,38 @@ ChunkArgs make_pass(const gla_dims* d, const gla_tensor* qr, const gla_tensor* k
   return a;
 }
 
+// Device address of `scratch` on the device that runs `stream`, looked up
+// once per device with that device current and kept for later calls.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+gla_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1, cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GLA_ERR_HIP;
+  dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return GLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return GLA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return GLA_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return GLA_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return GLA_OK;
+}
+
+// Validation and launch of the chunked forward.  The segment states live in
+// the caller's workspace (ws, ws_bytes), or, with noalloc, in the device's
+// static scratch.
+gla_status chunk_fwd_impl(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                          const gla_tensor* v, const float* lambda, const float* S0, gla_tensor* o,
+                          float* S_T, void* ws, size_t ws_bytes, bool noalloc, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -151,35 +193,13 @@ size_t gla_chunk_bwd_workspace(const gla_dims* dims) {
 gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
                          const gla_tensor* v, const float* lambda, const float* S0,
                          gla_tensor* o, float* S_T, void* ws, size_t ws_bytes, void* stream) {
-  if (!dims || !q || !k || !v || !o || !lambda) return GLA_ERR_NULL;
-  gla_status st = check_dims(dims);
-  if (st != GLA_OK) return st;
-  const int64_t B = dims->B, H = dims->H, T = dims->T;
-  if (!dtype_ok(q->dtype) || !dtype_ok(o->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
-    return GLA_ERR_DTYPE;
-  const int in_f32 = q->dtype == GLA_F32;
-  if (!gla::chunk_pass_supported((int)dims->dk, (int)dims->dv, (int)dims->chunk, in_f32))
-    return GLA_ERR_UNSUPPORTED;
-  const bool need = T > 0;
-  const int64_t DK = dims->dk, DV = dims->dv, C = dims->chunk;
-  if ((st = check_view(q, B, H, T, DK, C, need)) != GLA_OK) return st;
-  if ((st = check_view(k, B, H, T, DK, C, need)) != GLA_OK) return st;
-  if ((st = check_view(v, B, H, T, DV, C, need)) != GLA_OK) return st;
-  if ((st = check_view(o, B, H, T, DV, C, need)) != GLA_OK) return st;
-  if (!aligned16(S0) || !aligned16(S_T) || !aligned16(lambda)) return GLA_ERR_STRIDE;
-  if (same(o->data, q->data) || same(o->data, k->data) || same(o->data, v->data) ||
-      same(S_T, S0) || same(S_T, q->data) || same(S_T, k->data) || same(S_T, v->data) ||
-      same(S_T, o->data) || same(S_T, lambda) || same(o->data, lambda) || same(o->data, S0))
-    return GLA_ERR_ALIAS;
-  const size_t need_ws = gla_chunk_fwd_workspace(dims);
-  if (ws_bytes < need_ws || (need_ws > 0 && (ws == nullptr || !aligned16(ws)))) return GLA_ERR_WORKSPACE;
+  return chunk_fwd_impl(dims, q, k, v, lambda, S0, o, S_T, ws, ws_bytes, false, stream);
+}
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, o, 0);
-  set_segments(a, dims, (int)dims->dk, (int)dims->dv, ws);
-  if (gla::launch_chunk_pass((int)dims->dk, (int)dims->dv, (int)dims->chunk, a, s) != hipSuccess)
-    return GLA_ERR_HIP;
-  return GLA_OK;
+gla_status gla_chunk_fwd_noalloc(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                                 const gla_tensor* v, const float* lambda, const float* S0,
+                                 gla_tensor* o, float* S_T, void* stream) {
+  return chunk_fwd_impl(dims, q, k, v, lambda, S0, o, S_T, nullptr, 0, true, stream);
 }
 
 gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
@@ -492,3 +512,49 @@ gla_status gla_conv1d_step(int64_t N, int64_t D, const gla_tensor* x, const floa
 }
 
 }  // extern "C"
+
+namespace {
+
+gla_status chunk_fwd_impl(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                          const gla_tensor* v, const float* lambda, const float* S0, gla_tensor* o,
+                          float* S_T, void* ws, size_t ws_bytes, bool noalloc, void* stream) {
+  if (!dims || !q || !k || !v || !o || !lambda) return GLA_ERR_NULL;
+  gla_status st = check_dims(dims);
+  if (st != GLA_OK) return st;
+  const int64_t B = dims->B, H = dims->H, T = dims->T;
+  if (!dtype_ok(q->dtype) || !dtype_ok(o->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
+    return GLA_ERR_DTYPE;
+  const int in_f32 = q->dtype == GLA_F32;
+  if (!gla::chunk_pass_supported((int)dims->dk, (int)dims->dv, (int)dims->chunk, in_f32))
+    return GLA_ERR_UNSUPPORTED;
+  const bool need = T > 0;
+  const int64_t DK = dims->dk, DV = dims->dv, C = dims->chunk;
+  if ((st = check_view(q, B, H, T, DK, C, need)) != GLA_OK) return st;
+  if ((st = check_view(k, B, H, T, DK, C, need)) != GLA_OK) return st;
+  if ((st = check_view(v, B, H, T, DV, C, need)) != GLA_OK) return st;
+  if ((st = check_view(o, B, H, T, DV, C, need)) != GLA_OK) return st;
+  if (!aligned16(S0) || !aligned16(S_T) || !aligned16(lambda)) return GLA_ERR_STRIDE;
+  if (same(o->data, q->data) || same(o->data, k->data) || same(o->data, v->data) ||
+      same(S_T, S0) || same(S_T, q->data) || same(S_T, k->data) || same(S_T, v->data) ||
+      same(S_T, o->data) || same(S_T, lambda) || same(o->data, lambda) || same(o->data, S0))
+    return GLA_ERR_ALIAS;
+  const size_t need_ws = gla_chunk_fwd_workspace(dims);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (noalloc) {
+    // the segment states must fit the static scratch; nothing in it needs to
+    // start at zero (the state pass writes every entry the full pass reads)
+    if (need_ws > GLA_NOALLOC_SCRATCH_BYTES) return GLA_ERR_WORKSPACE;
+    ws = nullptr;
+    if (need_ws > 0 && (st = noalloc_scratch(s, &ws)) != GLA_OK) return st;
+  } else if (ws_bytes < need_ws || (need_ws > 0 && (ws == nullptr || !aligned16(ws)))) {
+    return GLA_ERR_WORKSPACE;
+  }
+
+  ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, o, 0);
+  set_segments(a, dims, (int)dims->dk, (int)dims->dv, ws);
+  if (gla::launch_chunk_pass((int)dims->dk, (int)dims->dv, (int)dims->chunk, a, s) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+}  // namespace

@@ -30,7 +30,9 @@
  *               enqueued; on a non-OK status nothing was enqueued.  A launch
  *               failure returns GLA_ERR_HIP.  Faults inside kernels surface at
  *               the caller's next synchronisation.  No C++ exception crosses
- *               the ABI.  Calls keep no global state and are thread-safe.
+ *               the ABI.  Calls keep no global state and are thread-safe,
+ *               except gla_chunk_fwd_noalloc, whose device scratch is
+ *               shared by every call on one GPU.
  *   Tensors     gla_tensor describes a 4-D (b, h, t, d) view: element
  *               (b, h, t, d) lives at data + (b*stride_b + h*stride_h +
  *               t*stride_t + d) elements; d is contiguous.  Strides are in
@@ -123,6 +125,31 @@ size_t gla_chunk_fwd_workspace(const gla_dims* dims);
 gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
                          const gla_tensor* v, const float* lambda, const float* S0,
                          gla_tensor* o, float* S_T, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch that gla_chunk_fwd_noalloc uses in
+ * place of a workspace (16 MiB per GPU). */
+#define GLA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* gla_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as gla_chunk_fwd, without ws/ws_bytes:
+ * the segment states go to a library-owned static array of
+ * GLA_NOALLOC_SCRATCH_BYTES on the device that runs `stream` (each GPU keeps
+ * its copy until the process ends; its address is looked up once per device
+ * on the first call there).  The call allocates nothing: it makes no
+ * hipMalloc/hipFree or allocating library call.
+ *   Limit   dims whose gla_chunk_fwd_workspace() exceeds the scratch return
+ *           GLA_ERR_WORKSPACE before anything is enqueued; at dk=96, dv=192
+ *           that is B*H in 114..127 with T of at least 4 chunks (254 segment
+ *           states of 73,728 bytes at most, against 227 that fit).
+ *   Sharing Every call on one GPU uses the same scratch: calls that overlap
+ *           on that GPU (different streams or host threads without ordering)
+ *           race and must be serialised by the caller.  Calls ordered on one
+ *           stream are safe; nothing in the scratch needs to start at zero,
+ *           since each call writes every entry before reading it. */
+gla_status gla_chunk_fwd_noalloc(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
+                                 const gla_tensor* v, const float* lambda, const float* S0,
+                                 gla_tensor* o, float* S_T, void* stream);
 
 /* Bytes of device workspace gla_chunk_bwd needs (0 if none): the largest
  * segment-state buffer of its three passes (see gla_chunk_fwd_workspace). */

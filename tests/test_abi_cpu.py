@@ -169,6 +169,34 @@ def test_fwd_workspace_checks(lib):
     assert fwd(lib, d, q, k, v, o, ws=0x800008, nws=need) == WS          # misaligned
 
 
+def fwd_noalloc(lib, d, q, k, v, o, lam=0x9000, S0=None, ST=None):
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    return lib.gla_chunk_fwd_noalloc(ref(d), ref(q), ref(k), ref(v), lam, S0, ref(o), ST, None)
+
+
+def test_fwd_noalloc_validation(lib):
+    """The allocation-free forward validates like gla_chunk_fwd, and rejects
+    dims whose segment states exceed its 16 MiB static scratch before any HIP
+    call: B*H = 120 at (96, 192) over 4 chunks needs 240 states of 73,728 B."""
+    assert lib.gla_chunk_fwd_noalloc.restype is ctypes.c_int
+    q, k, v, o = views(H=120, Tn=256)
+    d = dims(H=120, Tn=256, chunk=64)
+    need = lib.gla_chunk_fwd_workspace(ctypes.byref(d))
+    assert need == 120 * 2 * 96 * 192 * 4 > 16 << 20
+    assert fwd_noalloc(lib, d, q, k, v, o) == WS
+    # the largest B*H that still fits: 113 heads, 226 states
+    q2, k2, v2, o2 = views(H=113, Tn=256)
+    d2 = dims(H=113, Tn=256, chunk=64)
+    assert lib.gla_chunk_fwd_workspace(ctypes.byref(d2)) == 226 * 96 * 192 * 4 <= 16 << 20
+    # ordinary validation comes first and is the same as gla_chunk_fwd's
+    assert fwd_noalloc(lib, None, q, k, v, o) == NULL
+    assert fwd_noalloc(lib, d, q, k, v, o, lam=None) == NULL
+    assert fwd_noalloc(lib, dims(B=0), q, k, v, o) == SHAPE
+    assert fwd_noalloc(lib, dims(H=120, Tn=256, chunk=48), q, k, v, o) == UNSUP
+    o.data = q.data
+    assert fwd_noalloc(lib, d, q, k, v, o) == ALIAS
+
+
 def bwd(lib, d, q, k, v, dO, dq, dk, dv, lam=0x9000, S0=None, dST=None, dS0=None):
     ref = lambda x: None if x is None else ctypes.byref(x)
     return lib.gla_chunk_bwd(ref(d), ref(q), ref(k), ref(v), lam, S0, ref(dO), dST,
