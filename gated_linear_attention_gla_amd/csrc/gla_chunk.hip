@@ -216,7 +216,14 @@ struct ChunkLds {
   static constexpr int P_ELEMS = NTP * CP * PP;
   // When the four tiles do not fit, P is held in registers until every read
   // of the query tile is done and then written over it.
-  static constexpr int SEPARATE_BYTES = 2 * (Q_ELEMS + K_ELEMS + V_ELEMS + P_ELEMS) + 4 * (3 * CP + 2);
+  // Row-split passes (more waves than 16-column strips: RS waves share each
+  // strip, each owning DK / RS state rows) sum their partial readouts
+  // through an fp32 exchange tile of CP rows x BN columns.
+  static constexpr int RS = NW * 16 > BN ? NW * 16 / BN : 1;
+  static constexpr int XP = BN + 4;  // exchange row pitch (floats)
+  static constexpr int XCH_BYTES = RS > 1 ? 4 * CP * XP : 0;
+  static constexpr int SEPARATE_BYTES =
+      2 * (Q_ELEMS + K_ELEMS + V_ELEMS + P_ELEMS) + 4 * (3 * CP + 2) + XCH_BYTES;
   static constexpr bool ALIAS_P = SEPARATE_BYTES > 160 * 1024 - 512;
   // output staging (see the store stage): CP rows of BN values at pitch OP2
   // (bf16) or OP4 (fp32)
@@ -229,7 +236,8 @@ struct ChunkLds {
   static constexpr int P_REGION = P_ELEMS > STG_ELEMS ? P_ELEMS : STG_ELEMS;
   static constexpr bool STG_IN_P =
       !ALIAS_P && (STG_ELEMS <= P_ELEMS ||
-                   2 * (Q_ELEMS + K_ELEMS + V_ELEMS + P_REGION) + 4 * (3 * CP + 2) <= 160 * 1024 - 8192);
+                   2 * (Q_ELEMS + K_ELEMS + V_ELEMS + P_REGION) + 4 * (3 * CP + 2) + XCH_BYTES <=
+                       160 * 1024 - 8192);
   static constexpr int QP_RAW = ALIAS_P ? (Q_ELEMS > P_ELEMS ? Q_ELEMS : P_ELEMS)
                                         : Q_ELEMS + (STG_IN_P ? P_REGION : P_ELEMS);
   static constexpr int QP_ELEMS = QP_RAW > STG_ELEMS ? QP_RAW : STG_ELEMS;
@@ -246,7 +254,8 @@ struct ChunkLds {
   static constexpr int OFF_SQ = OFF_GP + (EPI ? 4 * CP * (DK / 8) : 0);
   static constexpr int OFF_GATE = OFF_SQ + (EPI ? 4 * CP * NWP : 0);
   static constexpr int OFF_AUG = OFF_GATE + (EPI ? 4 * CP : 0);
-  static constexpr int BYTES = OFF_AUG + (EPI ? 4 * DK : 0);
+  static constexpr int OFF_XCH = (OFF_AUG + (EPI ? 4 * DK : 0) + 15) / 16 * 16;
+  static constexpr int BYTES = OFF_XCH + XCH_BYTES;
   static_assert(OFF_K % 16 == 0 && OFF_V % 16 == 0 && OFF_POW % 16 == 0, "LDS regions must stay aligned");
 };
 
@@ -258,8 +267,14 @@ template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool
 __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, char* const smem) {
   using Lds = ChunkLds<DK, BN, C, NT, NW, EPI>;
   constexpr int NTHR = NW * 64;
-  constexpr int NS = BN / (16 * NW);  // 16-column strips per wave
-  static_assert(NS >= 1 && NS * 16 * NW == BN, "BN must split into 16-wide strips per wave");
+  // Row split (RS > 1): RS waves share each 16-column strip, wave half rh
+  // owning state rows [rh DK / RS, (rh + 1) DK / RS) -- their readouts are
+  // partial sums over those rows, combined through LDS, and the chunk's row
+  // tiles (intra term, output) are divided between them.
+  constexpr int RS = Lds::RS;
+  constexpr int NWS = NW / RS;         // waves per row half (strip owners)
+  constexpr int NS = BN / (16 * NWS);  // 16-column strips per wave
+  static_assert(NS >= 1 && NS * 16 * NWS == BN && NWS * RS == NW, "BN must split into 16-wide strips per wave");
   static_assert(DV % BN == 0, "DV must be a multiple of BN");
   static_assert(DK % 16 == 0 && C % 16 == 0, "dims must be multiples of 16");
   constexpr int NBLK = DV / BN;
@@ -276,6 +291,12 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   constexpr int PP = Lds::PP;
   constexpr int DKT = DK / 16;  // 16-row tiles of the state
   constexpr int KSD = DKP / 32;  // 32-deep k-steps over DK
+  constexpr int DKTO = DKT / RS;  // state row tiles owned by one wave
+  constexpr int KSDO = KSD / RS;  // readout k-steps of one wave
+  static_assert(RS == 1 || (DK % (32 * RS) == 0 && DKTO * RS == DKT && KSDO * RS == KSD),
+                "a row split must give each half whole 32-row k-steps");
+  static_assert(RS <= 2, "row tiles are divided between two halves");
+  static_assert(RS == 1 || !EPI, "the fused epilogue needs whole rows per wave");
   constexpr int CT = CP / 16;    // 16-row tiles of a chunk
   constexpr int KSC = CP / 32;   // 32-deep k-steps over the chunk
   constexpr int NPT = CT * (CT + 1) / 2;  // causal P tiles
@@ -382,6 +403,12 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int rh = RS > 1 ? w / NWS : 0;                      // row half (row-split passes)
+  const int ws = RS > 1 ? w - rh * NWS : w;                 // strip-owner index
+  // Row-split passes divide the chunk's row tiles between the two halves,
+  // alternating in pairs (0 and 3 to one half, 1 and 2 to the other, ...),
+  // which balances the causal intra work: row tile I meets I / 2 + 1 k-steps.
+  auto own_row = [&](int I) { return RS == 1 || (((I + (I >> 1)) & 1) == rh); };
   const int l = tid & 63;
   const int g = l >> 4;
   const int li = l & 15;
@@ -398,7 +425,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gam[s][r] = a.gamma[h * DV + (w * NS + s) * 16 + 4 * g + r];
+      for (int r = 0; r < 4; ++r) gam[s][r] = a.gamma[h * DV + (ws * NS + s) * 16 + 4 * g + r];
   }
   // (reads sPow: every call site is preceded by a barrier after sPow is filled)
   auto fill_factors = [&](int Lc) {
@@ -429,23 +456,25 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   const int64_t q_off = b * a.sq_b + h * a.sq_h + tbase * a.sq_t;
   const int64_t k_off = b * a.sk_b + h * a.sk_h + tbase * a.sk_t;
   const int64_t v_off = b * a.sv_b + h * a.sv_h + tbase * a.sv_t + (int64_t)nblk * BN;
-  const int col0 = nblk * BN + w * NS * 16 + li;  // + 16 s: this lane's column in strip s
+  const int col0 = nblk * BN + ws * NS * 16 + li;  // + 16 s: this lane's column in strip s
 
-  // ---- state slice in accumulators: accS[D][s][r] = S[16 D + 4 g + r][col0 + 16 s]
-  f32x4 accS[DKT][NS];
+  // ---- state slice in accumulators: accS[Do][s][r] = S[state_row(D)][col0 + 16 s]
+  // for this wave's row tiles D = rh DKTO + Do
+  f32x4 accS[DKTO][NS];
   {
     const float* si = SO ? nullptr : s_init;
 #pragma unroll
-    for (int D = 0; D < DKT; ++D)
+    for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          const int D = rh * DKTO + Do;
           const int d = state_row<DK>(D, g, r);
           const int n = col0 + 16 * s;
           float x = 0.0f;
           if (si) x = a.s_init_trans ? si[(int64_t)n * DK + d] : si[(int64_t)d * DV + n];
-          accS[D][s][r] = x;
+          accS[Do][s][r] = x;
         }
   }
   // The segments before this one (in walk order) enter through their end
@@ -458,12 +487,13 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       const float dec = lam_pow_f32(a.lam[h], (int)len);
       const float* E = a.seg_state + (bh * nseg + p) * (int64_t)DK * DV;
 #pragma unroll
-      for (int D = 0; D < DKT; ++D)
+      for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            accS[D][s][r] = fmaf(dec, accS[D][s][r], E[(int64_t)state_row<DK>(D, g, r) * DV + col0 + 16 * s]);
+            accS[Do][s][r] =
+                fmaf(dec, accS[Do][s][r], E[(int64_t)state_row<DK>(rh * DKTO + Do, g, r) * DV + col0 + 16 * s]);
     }
   }
 
@@ -525,6 +555,42 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     pfk.load(kb + (k_off + t0 * a.sk_t) * esz, (uint32_t)a.sk_t, Ln, tid);
     pfv.load(vb + (v_off + t0 * a.sv_t) * esz, (uint32_t)a.sv_t, Ln, tid);
   };
+  // Stores a staged output chunk (tokens [t0s, t0s + Ls) of this unit's
+  // column block) with coalesced 16-byte row writes.  accO held O^T tiles:
+  // lane (g, li) had row 16 I + li, columns strip + 4 g .. + 3, and the
+  // staging buffer holds them row-major.  The buffer resource ends at the
+  // last valid row, so stores of rows >= Ls are dropped by the hardware
+  // range check.
+  auto store_out = [&](const bf16_t* stg, int64_t t0s, int Ls) {
+    const int f32o = a.o_f32;
+    const int oes = f32o ? 4 : 2;
+    char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + (tbase + t0s) * a.so_t + nblk * BN) * oes;
+    const uint32_t so_t = (uint32_t)a.so_t;
+    const uint32_t nbytes = ((uint32_t)(Ls - 1) * so_t + BN) * oes;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)nbytes, 0x00020000);
+    // thread tid stores column vector tid % VPR of rows tid / VPR + RPJ j
+    auto store_rows = [&](auto vpr_c, auto es_c) {
+      constexpr int VPR = decltype(vpr_c)::value;  // 16-byte vectors per row
+      constexpr int ES = decltype(es_c)::value;
+      static_assert(NTHR % VPR == 0, "threads must cover whole rows");
+      constexpr int RPJ = NTHR / VPR;
+      constexpr int PITCH_B = ES == 4 ? OP4 * 4 : OP2 * 2;  // staging pitch in bytes
+      const int row0 = tid / VPR;
+      const int cv = tid - row0 * VPR;
+      const char* src = reinterpret_cast<const char*>(stg) + row0 * PITCH_B + cv * 16;
+      const uint32_t voff = (uint32_t)row0 * so_t * ES + cv * 16;
+#pragma unroll
+      for (int j = 0; j < (CP + RPJ - 1) / RPJ; ++j) {
+        if (CP % RPJ == 0 || row0 + j * RPJ < CP) {
+          const u32x4 val = *reinterpret_cast<const u32x4*>(src + j * RPJ * PITCH_B);
+          __builtin_amdgcn_raw_buffer_store_b128(val, rs, voff, (int)((uint32_t)(j * RPJ) * so_t * ES), 0);
+        }
+      }
+    };
+    if (f32o) store_rows(std::integral_constant<int, BN * 4 / 16>{}, std::integral_constant<int, 4>{});
+    else store_rows(std::integral_constant<int, BN * 2 / 16>{}, std::integral_constant<int, 2>{});
+  };
+
   // Chunk pipeline.  The tiles of chunk ci+1 are loaded into registers while
   // chunk ci is computed and written to LDS as soon as its last reader is
   // done; the output of chunk ci is stored last, so its write latency
@@ -638,18 +704,20 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       for (int s = 0; s < NS; ++s) accO[I][s] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (!SO) {
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
+    for (int kso = 0; kso < KSDO; ++kso) {
       // State as the B operand of Q S: k-slot e of lane group g takes
       // accumulator slot e % 4 of row tile 2 ks + e / 4, i.e. state row
       // state_row(2 ks + e / 4, g, e % 4); Q is read at the same rows
-      // (32 ks + 8 g + e when DK is a multiple of 32).
+      // (32 ks + 8 g + e when DK is a multiple of 32).  A row-split wave
+      // covers only its own k-steps.
+      const int ks = rh * KSDO + kso;
       bf16x8 Sf[NS][NTS];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int D = 2 * ks + (e >> 2);
-          const float x = (D < DKT) ? accS[D < DKT ? D : 0][s][e & 3] : 0.0f;
+          const int Do = 2 * kso + (e >> 2);
+          const float x = (Do < DKTO) ? accS[Do < DKTO ? Do : 0][s][e & 3] : 0.0f;
           __bf16 t[NTS];
           split_terms<NTS>(x, t);
 #pragma unroll
@@ -676,11 +744,11 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     {
       const float cfac = sPow[L];
 #pragma unroll
-      for (int D = 0; D < DKT; ++D)
+      for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) accS[D][s][r] *= cfac;
+          for (int r = 0; r < 4; ++r) accS[Do][s][r] *= cfac;
       if constexpr (!SO) {
 #pragma unroll
         for (int I = 0; I < CT; ++I) {
@@ -694,6 +762,18 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       }
     }
 
+    // row split: hand the partial readout of the other half's row tiles over
+    float* const sX = reinterpret_cast<float*>(smem + Lds::OFF_XCH);
+    if constexpr (RS > 1 && !SO) {
+#pragma unroll
+      for (int I = 0; I < CT; ++I) {
+        if (own_row(I)) continue;
+        const int row = 16 * (rev ? CT - 1 - I : I) + li;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          *reinterpret_cast<f32x4*>(&sX[row * Lds::XP + (ws * NS + s) * 16 + 4 * g]) = accO[I][s];
+      }
+    }
     if constexpr (ALIAS_P && !SO) {
       __syncthreads();  // every read of the query tile is done
 #pragma unroll
@@ -734,11 +814,25 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         sGP[u] = sacc;
       }
     }
-    if constexpr (!SO) __syncthreads();  // P complete
+    if constexpr (!SO) __syncthreads();  // P complete (and the readout hand-over)
     // wide query rows: the next query tile is fetched now, once the readout's
     // registers are free, and written to LDS at the end of the chunk
     if constexpr (LATE_Q && !SO) {
       if (ci + 1 < nchunks) prefetch_q(ci + 1);
+    }
+    // row split: add the other half's partial readout of this wave's row tiles
+    if constexpr (RS > 1 && !SO) {
+#pragma unroll
+      for (int I = 0; I < CT; ++I) {
+        if (!own_row(I)) continue;
+        const int row = 16 * (rev ? CT - 1 - I : I) + li;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(&sX[row * Lds::XP + (ws * NS + s) * 16 + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accO[I][s][r] += t[r];
+        }
+      }
     }
     if constexpr (EPI && !SO) {
       for (int row = tid; row < CP; row += NTHR) {
@@ -759,7 +853,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         // rows 32 ks + 8 g + (0..7): bit 3 is that of 8 g
-        const int c0 = ((w * NS + s) * 16 + 4 * (li & 3)) ^ (SWV ? tile_swz(8 * g) : 0);
+        const int c0 = ((ws * NS + s) * 16 + 4 * (li & 3)) ^ (SWV ? tile_swz(8 * g) : 0);
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
           const bf16_t* base = &sV[p * CP * PVV + (32 * ks + 8 * g + (li >> 2)) * PVV + c0];
@@ -769,7 +863,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       // stage 3 for the row tiles whose causal window touches this k-step
 #pragma unroll
       for (int I = 0; I < CT; ++I) {
-        if (SO || kl > (I >> 1)) continue;
+        if (SO || kl > (I >> 1) || !own_row(I)) continue;
         const int Iph = rev ? CT - 1 - I : I;
         bf16x8 Ap[NTP];
 #pragma unroll
@@ -800,7 +894,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           }
       }
 #pragma unroll
-      for (int D = 0; D < DKT; ++D) {
+      for (int Do = 0; Do < DKTO; ++Do) {
+        const int D = rh * DKTO + Do;  // this wave's state row tiles
         // keys as the A operand, A[m = d][k = j], via column reads
         bf16x8 Ak[NT];
 #pragma unroll
@@ -813,7 +908,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           Ak[p] = cat4(lds_read_tr(base), lds_read_tr(base + 4 * PK));
         }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) mma_split<NT, NTK>(accS[D][s], Ak, Bs[s]);
+        for (int s = 0; s < NS; ++s) mma_split<NT, NTK>(accS[Do][s], Ak, Bs[s]);
         // where registers are tight, keep the scheduler from hoisting every
         // tile's loads at once
         if constexpr (TIGHT) __builtin_amdgcn_sched_barrier(0);
@@ -843,7 +938,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 #pragma unroll
           for (int p = 0; p < NT; ++p) {
             const bf16x4 t = lds_read_b64(&sV[p * CP * PVV + (16 * I + li) * PVV +
-                                              (((w * NS + s) * 16 + 4 * g) ^ (SWV ? tile_swz(li) : 0))]);
+                                              (((ws * NS + s) * 16 + 4 * g) ^ (SWV ? tile_swz(li) : 0))]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) vreg[I][s][r] += bf16v_to_f32(t[r]);
           }
@@ -862,6 +957,33 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     const bool more = ci + 1 < nchunks;
     // the factor tables change only when the next chunk's length differs
     const bool refill = more && chunk_len(chunk_start(ci + 1)) != L;
+    // this wave's output rows into the staging buffer: fp32, or bf16 rounded
+    // to nearest
+    auto stage_out = [&](bf16_t* stg) {
+      if (a.o_f32) {
+        float* st4 = reinterpret_cast<float*>(stg);
+#pragma unroll
+        for (int I = 0; I < CT; ++I) {
+          if (!own_row(I)) continue;
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            *reinterpret_cast<f32x4*>(&st4[(16 * (rev ? CT - 1 - I : I) + li) * OP4 + (ws * NS + s) * 16 + 4 * g]) =
+                accO[I][s];
+        }
+      } else {
+#pragma unroll
+        for (int I = 0; I < CT; ++I) {
+          if (!own_row(I)) continue;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            bf16x4 pk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pk[r] = (__bf16)accO[I][s][r];
+            *reinterpret_cast<bf16x4*>(&stg[(16 * (rev ? CT - 1 - I : I) + li) * OP2 + (ws * NS + s) * 16 + 4 * g]) = pk;
+          }
+        }
+      }
+    };
     if (more) {
       pfk.store(sK, tid);
       pfv.store(sV, tid);
@@ -933,7 +1055,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           f32x4 y;
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = accO[I][s][r] * rstd * gam[s][r];
-          *reinterpret_cast<f32x4*>(&st4[row * OP4 + (w * NS + s) * 16 + 4 * g]) = y;
+          *reinterpret_cast<f32x4*>(&st4[row * OP4 + (ws * NS + s) * 16 + 4 * g]) = y;
         }
       }
       __syncthreads();
@@ -982,53 +1104,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         }
       }
     } else if constexpr (!SO) {
-      const int f32o = a.o_f32;
       bf16_t* stg = STG_IN_P ? sP : sQP;
-      if (f32o) {
-        float* st4 = reinterpret_cast<float*>(stg);
-#pragma unroll
-        for (int I = 0; I < CT; ++I)
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-            *reinterpret_cast<f32x4*>(&st4[(16 * (rev ? CT - 1 - I : I) + li) * OP4 + (w * NS + s) * 16 + 4 * g]) = accO[I][s];
-      } else {
-#pragma unroll
-        for (int I = 0; I < CT; ++I)
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            bf16x4 pk;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pk[r] = (__bf16)accO[I][s][r];
-            *reinterpret_cast<bf16x4*>(&stg[(16 * (rev ? CT - 1 - I : I) + li) * OP2 + (w * NS + s) * 16 + 4 * g]) = pk;
-          }
-      }
+      stage_out(stg);
       __syncthreads();
-      const int oes = f32o ? 4 : 2;
-      char* obase = reinterpret_cast<char*>(a.o) + (b * a.so_b + h * a.so_h + (tbase + t0) * a.so_t + nblk * BN) * oes;
-      const uint32_t so_t = (uint32_t)a.so_t;
-      const uint32_t nbytes = ((uint32_t)(L - 1) * so_t + BN) * oes;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)nbytes, 0x00020000);
-      // thread tid stores column vector tid % VPR of rows tid / VPR + RPJ j
-      auto store_rows = [&](auto vpr_c, auto es_c) {
-        constexpr int VPR = decltype(vpr_c)::value;  // 16-byte vectors per row
-        constexpr int ES = decltype(es_c)::value;
-        static_assert(NTHR % VPR == 0, "threads must cover whole rows");
-        constexpr int RPJ = NTHR / VPR;
-        constexpr int PITCH_B = ES == 4 ? OP4 * 4 : OP2 * 2;  // staging pitch in bytes
-        const int row0 = tid / VPR;
-        const int cv = tid - row0 * VPR;
-        const char* src = reinterpret_cast<const char*>(stg) + row0 * PITCH_B + cv * 16;
-        const uint32_t voff = (uint32_t)row0 * so_t * ES + cv * 16;
-#pragma unroll
-        for (int j = 0; j < (CP + RPJ - 1) / RPJ; ++j) {
-          if (CP % RPJ == 0 || row0 + j * RPJ < CP) {
-            const u32x4 val = *reinterpret_cast<const u32x4*>(src + j * RPJ * PITCH_B);
-            __builtin_amdgcn_raw_buffer_store_b128(val, rs, voff, (int)((uint32_t)(j * RPJ) * so_t * ES), 0);
-          }
-        }
-      };
-      if (f32o) store_rows(std::integral_constant<int, BN * 4 / 16>{}, std::integral_constant<int, 4>{});
-      else store_rows(std::integral_constant<int, BN * 2 / 16>{}, std::integral_constant<int, 2>{});
+      store_out(stg, t0, L);
     }
     if constexpr (!STG_IN_P) {
       __syncthreads();  // the staged output has been read
@@ -1047,11 +1126,12 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   if (dst) {
     float* sf = dst;
 #pragma unroll
-    for (int D = 0; D < DKT; ++D)
+    for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sf[(int64_t)state_row<DK>(D, g, r) * DV + col0 + 16 * s] = accS[D][s][r];
+        for (int r = 0; r < 4; ++r)
+          sf[(int64_t)state_row<DK>(rh * DKTO + Do, g, r) * DV + col0 + 16 * s] = accS[Do][s][r];
   }
 }
 
@@ -1215,9 +1295,12 @@ template <int DK, int DV, int C, int NT>
 static hipError_t launch_shape(const ChunkArgs& a, const ChunkArgs* a1, hipStream_t st) {
   if constexpr (DK == 96 && DV == 192) return launch_tiles<96, 192, 96, 6, C, NT>(a, a1, st);
   else if constexpr (DK == 192 && DV == 96) {
-    // all 96 columns on 6 waves (registers allow it up to 64-token chunks),
-    // else 48 columns on 3 waves with the wider register budget
-    if constexpr (C <= 64) return launch_tiles<192, 96, 96, 6, C, NT>(a, a1, st);
+    // bf16 inputs up to 64-token chunks: all 96 columns on 12 waves, each
+    // 16-column strip shared by two waves that own 96 state rows each (three
+    // waves on every SIMD); fp32 inputs: 96 columns on 6 waves; 128-token
+    // chunks: 48 columns on 3 waves with the wider register budget
+    if constexpr (C <= 64 && NT == 1) return launch_tiles<192, 96, 96, 12, C, NT>(a, a1, st);
+    else if constexpr (C <= 64) return launch_tiles<192, 96, 96, 6, C, NT>(a, a1, st);
     else return launch_tiles<192, 96, 48, 3, C, NT>(a, a1, st);
   }
   else if constexpr (DK == 16 && DV == 32) return launch_tiles<16, 32, 32, 2, C, NT>(a, a1, st);
