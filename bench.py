@@ -266,10 +266,17 @@ def bench_decode(gla, inputs, steps_override=None):
     aug = torch.zeros((H, DK), dtype=torch.float32, device="cuda")
     gam = torch.ones((H, DV), dtype=torch.float32, device="cuda")
     blk = qkv[0, 0]
+    lib = gla.load_library()
+    ws = torch.empty(lib.gla_decode_step_fused_workspace(N, H, DK, DV), dtype=torch.uint8, device="cuda")
     fused = lambda: gla.decode_step_fused_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, S[0], gz,
-                                           aug, gam, 1e-6, y=o)
+                                           aug, gam, 1e-6, y=o, ws=ws)
     warm_up(fused)
     fused_ms = event_time_ms(fused, 20, stream)
+    # the same without a workspace (one workgroup per state, row normalised in the kernel)
+    fused1 = lambda: gla.decode_step_fused_(blk[..., :DK], blk[..., DK:2 * DK], blk[..., 2 * DK:], lam, S[0], gz,
+                                            aug, gam, 1e-6, y=o, use_workspace=False)
+    warm_up(fused1)
+    fused1_ms = event_time_ms(fused1, 20, stream)
     # per-call samples: one step's 24 layer calls, each timed with its own events
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(Lyr)]
     for layer, (s1, e1) in enumerate(ev):
@@ -292,6 +299,7 @@ def bench_decode(gla, inputs, steps_override=None):
         hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         state_gb=S.numel() * 4 / 1e9,
         ms_per_layer_call_fused_epilogue=fused_ms,
+        ms_per_layer_call_fused_epilogue_no_workspace=fused1_ms,
         per_call=dict(ms_median=per[Lyr // 2], ms_min=per[0], calls=Lyr),
         stream_ceiling=dict(kernel="in-place scale of one layer's states (torch mul_)", gbs=scale_gbs,
                             decode_frac_of_it=(nbytes / (ms / 1e3) / 1e9) / scale_gbs),

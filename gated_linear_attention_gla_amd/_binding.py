@@ -103,11 +103,13 @@ def load_library(path=LIB_PATH):
     ]
     lib.gla_decode_workgroups_per_state.restype = ctypes.c_int
     lib.gla_decode_workgroups_per_state.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.gla_decode_step_fused_workspace.restype = ctypes.c_size_t
+    lib.gla_decode_step_fused_workspace.argtypes = [ctypes.c_int64] * 4
     lib.gla_decode_step_fused.restype = ctypes.c_int
     lib.gla_decode_step_fused.argtypes = [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp, ctypes.c_int64,
-        P(GlaTensor), vp, vp, ctypes.c_float, P(GlaTensor), vp,
+        P(GlaTensor), vp, vp, ctypes.c_float, P(GlaTensor), vp, ctypes.c_size_t, vp,
     ]
     lib.gla_chunk_fwd_fused_workspace.restype = ctypes.c_size_t
     lib.gla_chunk_fwd_fused_workspace.argtypes = [P(GlaDims)]
@@ -367,9 +369,13 @@ def chunk_fwd_fused(q, k, v, lam, g, aug, gamma, eps=1e-6, S0=None, chunk=64, ou
     return y, S_T
 
 
-def decode_step_fused_(q, k, v, lam, S, g, aug, gamma, eps=1e-6, y=None, out_dtype=None):
+def decode_step_fused_(q, k, v, lam, S, g, aug, gamma, eps=1e-6, y=None, out_dtype=None, ws=None,
+                       use_workspace=True):
     """y = decode_step_fused_(q, k, v, lam, S, g, aug, gamma, eps): one
-    recurrent step (S in place) with the output epilogue; g (N, H, dv)."""
+    recurrent step (S in place) with the output epilogue; g (N, H, dv).
+    ws: a uint8 device tensor of at least gla_decode_step_fused_workspace()
+    bytes, or None to allocate one (use_workspace=False runs the step
+    without a workspace)."""
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -388,10 +394,20 @@ def decode_step_fused_(q, k, v, lam, S, g, aug, gamma, eps=1e-6, y=None, out_dty
     _same_device(q, k, v, g, lam, S, y, aug, gamma)
     if y is None:
         y = torch.empty((N, H, dv), dtype=out_dtype or q.dtype, device=q.device)
+    nws = lib.gla_decode_step_fused_workspace(N, H, dk, dv) if use_workspace else 0
+    if nws and ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    if not nws:
+        ws = None
+    elif ws.dtype != torch.uint8 or ws.numel() < nws or not ws.is_contiguous():
+        raise ValueError(f"ws must be a contiguous uint8 tensor of at least {nws} bytes")
+    else:
+        _same_device(q, ws)
     tq, tk, tv, tg, ty = _view3(q), _view3(k), _view3(v), _view3(g), _view3(y)
     st = lib.gla_decode_step_fused(
         N, H, dk, dv, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(lam), _ptr(S), S.stride(0),
-        ctypes.byref(tg), _ptr(aug), _ptr(gamma), ctypes.c_float(eps), ctypes.byref(ty), _stream(),
+        ctypes.byref(tg), _ptr(aug), _ptr(gamma), ctypes.c_float(eps), ctypes.byref(ty), _ptr(ws),
+        nws, _stream(),
     )
     _check(lib, st)
     return y

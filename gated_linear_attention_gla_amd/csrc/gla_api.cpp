@@ -252,10 +252,18 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
   return GLA_OK;
 }
 
+// Workspace of the fused decode step: o' (fp32, N*H*dv) and the column
+// slices' sums of squares (4 floats per state), when the step runs as column
+// slices plus a normalisation kernel; 0 when it runs one workgroup per state.
+static size_t decode_fused_ws(int64_t N, int64_t H, int64_t dk, int64_t dv) {
+  if (gla::decode_slices(N * H, (int)dk, (int)dv, true, true) <= 1) return 0;
+  return (size_t)(N * H) * (size_t)(dv + 4) * sizeof(float);
+}
+
 static gla_status decode_impl(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
                               const gla_tensor* k, const gla_tensor* v, const float* lambda, float* S,
                               int64_t S_stride_n, const gla_tensor* g, const float* aug, const float* gamma,
-                              float eps, gla_tensor* o, void* stream) {
+                              float eps, gla_tensor* o, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !lambda || !S || !o) return GLA_ERR_NULL;
   // N * H <= 2^24 states: the launch (gla::decode_slices picks three column
   // slices per state while they fit, else one 192-thread workgroup per
@@ -282,6 +290,14 @@ static gla_status decode_impl(int64_t N, int64_t H, int64_t dk, int64_t dv, cons
     if (same(o->data, g->data) || same(o->data, aug) || same(o->data, gamma) || same(S, g->data) ||
         same(S, aug) || same(S, gamma))
       return GLA_ERR_ALIAS;
+    if (ws != nullptr) {
+      const size_t need = decode_fused_ws(N, H, dk, dv);
+      if (ws_bytes < need || !aligned16(ws)) return GLA_ERR_WORKSPACE;
+      const void* other[] = {q->data, k->data, v->data, g->data, lambda, aug, gamma, S, o->data};
+      for (const void* p : other)
+        if (same(ws, p)) return GLA_ERR_ALIAS;
+      if (need == 0) ws = nullptr;  // this shape runs one workgroup per state
+    }
   }
   if (!aligned16(S) || !aligned16(lambda) || (N > 1 && (S_stride_n * 4) % 16 != 0)) return GLA_ERR_STRIDE;
   const void* ins[] = {q->data, k->data, v->data, lambda};
@@ -309,6 +325,7 @@ static gla_status decode_impl(int64_t N, int64_t H, int64_t dk, int64_t dv, cons
     a.aug = aug;
     a.gamma = gamma;
     a.eps = eps;
+    a.ws = static_cast<float*>(ws);
   }
   if (gla::launch_decode((int)dk, (int)dv, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return GLA_ERR_HIP;
@@ -318,21 +335,29 @@ static gla_status decode_impl(int64_t N, int64_t H, int64_t dk, int64_t dv, cons
 gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
                            const gla_tensor* k, const gla_tensor* v, const float* lambda,
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream) {
-  return decode_impl(N, H, dk, dv, q, k, v, lambda, S, S_stride_n, nullptr, nullptr, nullptr, 0.0f, o, stream);
+  return decode_impl(N, H, dk, dv, q, k, v, lambda, S, S_stride_n, nullptr, nullptr, nullptr, 0.0f, o, nullptr, 0,
+                     stream);
 }
 
 int gla_decode_workgroups_per_state(int64_t N, int64_t H, int64_t dk, int64_t dv, int fused) {
   if (N < 1 || H < 1 || N > (int64_t)1 << 30 || H > (int64_t)1 << 16 || N * H > (int64_t)1 << 24) return 0;
+  if (dk < 1 || dv < 1 || dk > 4096 || dv > 4096 || fused < 0 || fused > 2) return 0;
+  return gla::decode_slices(N * H, (int)dk, (int)dv, fused != 0, fused == 1);
+}
+
+size_t gla_decode_step_fused_workspace(int64_t N, int64_t H, int64_t dk, int64_t dv) {
+  if (N < 1 || H < 1 || N > (int64_t)1 << 30 || H > (int64_t)1 << 16 || N * H > (int64_t)1 << 24) return 0;
   if (dk < 1 || dv < 1 || dk > 4096 || dv > 4096) return 0;
-  return gla::decode_slices(N * H, (int)dk, (int)dv, fused != 0);
+  return decode_fused_ws(N, H, dk, dv);
 }
 
 gla_status gla_decode_step_fused(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
                                  const gla_tensor* k, const gla_tensor* v, const float* lambda, float* S,
                                  int64_t S_stride_n, const gla_tensor* g, const float* aug,
-                                 const float* gamma, float eps, gla_tensor* y, void* stream) {
+                                 const float* gamma, float eps, gla_tensor* y, void* ws, size_t ws_bytes,
+                                 void* stream) {
   if (!g) return GLA_ERR_NULL;
-  return decode_impl(N, H, dk, dv, q, k, v, lambda, S, S_stride_n, g, aug, gamma, eps, y, stream);
+  return decode_impl(N, H, dk, dv, q, k, v, lambda, S, S_stride_n, g, aug, gamma, eps, y, ws, ws_bytes, stream);
 }
 
 size_t gla_chunk_fwd_fused_workspace(const gla_dims* dims) {

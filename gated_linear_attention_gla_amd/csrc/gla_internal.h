@@ -80,6 +80,9 @@ struct DecodeArgs {
   const float* aug;
   const float* gamma;
   float eps;
+  // fused step's workspace (split epilogue), or null: o' [N*H][DV] fp32, then
+  // the column slices' sums of squares [N*H][4]
+  float* ws;
 };
 
 // Depthwise causal convolution (width 4) + SiLU over [B][T][D] activations.
@@ -132,9 +135,10 @@ hipError_t launch_chunk_fused(int dk, int dv, int chunk, const ChunkArgs& a, hip
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
 bool decode_supported(int dk, int dv);
 // Workgroups (column slices) the decode step launches per state for `states`
-// states (0 when the shape has no kernel); the launch stays below 2^32
-// work-items for every state count the ABI accepts.
-int decode_slices(int64_t states, int dk, int dv, bool epi);
+// states (0 when the shape has no kernel), plain or fused (epi), the fused
+// step with or without its workspace; the launch stays below 2^32 work-items
+// for every state count the ABI accepts.
+int decode_slices(int64_t states, int dk, int dv, bool epi, bool has_ws);
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);
 hipError_t launch_conv_step(const ConvStepArgs& a, hipStream_t st);
 // one-dimensional grid sizes of the two convolution launches, and their

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 1
+#define GLA_ABI_VERSION 2
 
 typedef enum {
   GLA_OK = 0,
@@ -183,12 +183,14 @@ gla_status gla_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, const g
                            float* S, int64_t S_stride_n, gla_tensor* o, void* stream);
 
 /* Launch shape of the decode step, for capacity planning and tests (calling
- * it is never required): the number of workgroups gla_decode_step (fused = 0)
- * or gla_decode_step_fused (fused != 0) launches per (n, h) state for these
- * sizes, or 0 when that call would reject them.  The (96, 192) plain step
- * splits each state into 3 column slices while N * H * 3 * 384 work-items
- * fit one launch (up to 3,728,270 states), else it runs one workgroup per
- * state; the fused step always runs one workgroup per state. */
+ * it is never required): the number of workgroups gla_decode_step (fused =
+ * 0), gla_decode_step_fused with its workspace (fused = 1) or without one
+ * (fused = 2) launches per (n, h) state for these sizes, or 0 when that call
+ * would reject them (or fused is outside 0..2).  At (96, 192) the plain step
+ * and the fused step with its workspace split each state into 3 column
+ * slices while N * H * 3 * 384 work-items fit one launch (up to 3,728,270
+ * states), else they run one workgroup per state; the fused step without a
+ * workspace always runs one workgroup per state. */
 int gla_decode_workgroups_per_state(int64_t N, int64_t H, int64_t dk, int64_t dv, int fused);
 
 /* Chunked forward with the mixer's output epilogue fused into the store
@@ -215,15 +217,29 @@ gla_status gla_chunk_fwd_fused(const gla_dims* dims, const gla_tensor* q, const 
                                const gla_tensor* g, const float* aug, const float* gamma, float eps,
                                gla_tensor* y, float* S_T, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace gla_decode_step_fused can use for these sizes
+ * (0 when the step runs one workgroup per state anyway, or the sizes are
+ * rejected): N*H*(dv + 4) fp32 values at (96, 192). */
+size_t gla_decode_step_fused_workspace(int64_t N, int64_t H, int64_t dk, int64_t dv);
+
 /* gla_decode_step with the same output epilogue as gla_chunk_fwd_fused
  * applied to o before it is written (y replaces o):
  *   g      the gate stream [N, H, dv] view (stride_b steps n, stride_h h;
  *          same dtype as q, k, v)
- *   aug    fp32 [H][dk]; gamma fp32 [H][dv]; eps >= 0. */
+ *   aug    fp32 [H][dk]; gamma fp32 [H][dv]; eps >= 0
+ *   ws, ws_bytes  optional workspace of gla_decode_step_fused_workspace()
+ *          bytes, 16-byte aligned, not shared with any other argument
+ *          (GLA_ERR_WORKSPACE / GLA_ERR_ALIAS otherwise).  With it, the step
+ *          streams each state as column slices and normalises in a second
+ *          kernel (faster); with ws = NULL one workgroup owns each state and
+ *          normalises its row itself.  Both give the same state; outputs
+ *          agree up to the summation order of the sum of squares.  The
+ *          workspace is scratch, not needed after the call completes. */
 gla_status gla_decode_step_fused(int64_t N, int64_t H, int64_t dk, int64_t dv, const gla_tensor* q,
                                  const gla_tensor* k, const gla_tensor* v, const float* lambda, float* S,
                                  int64_t S_stride_n, const gla_tensor* g, const float* aug,
-                                 const float* gamma, float eps, gla_tensor* y, void* stream);
+                                 const float* gamma, float eps, gla_tensor* y, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Variable-length batched prefill straight into the decode state pool (page
  * sections "GLA mixer" and "Inference optimization on Trainium2": each

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gla_abi_version() == 1
+    assert lib.gla_abi_version() == 2
     for s in range(9):
         assert lib.gla_status_string(s)
     assert lib.gla_status_string(42) == b"unknown status"
@@ -266,7 +266,8 @@ def test_decode_validation(lib):
 def test_decode_launch_shape_boundary(lib):
     """The decode step's per-state workgroup count: three 384-thread column
     slices while N * H * 1152 work-items fit one launch (2^32 - 1), else one
-    workgroup per state; the fused step always one; 0 for rejected sizes."""
+    workgroup per state; the fused step the same with its workspace and one
+    without; 0 for rejected sizes."""
     f = lib.gla_decode_workgroups_per_state
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
@@ -277,8 +278,12 @@ def test_decode_launch_shape_boundary(lib):
     assert f(1 << 20, 4, 96, 192, 0) == 1  # 2^22 states: the old guard's bound, now one workgroup each
     assert f(1 << 24, 1, 96, 192, 0) == 1  # the largest N * H gla_decode_step accepts
     assert f((1 << 24) + 1, 1, 96, 192, 0) == 0
-    assert f(1280, 16, 96, 192, 1) == 1
+    assert f(1280, 16, 96, 192, 1) == 3  # fused step with its workspace: the same slices
+    assert f(3_728_271, 1, 96, 192, 1) == 1
+    assert f(1280, 16, 96, 192, 2) == 1  # fused step without a workspace
+    assert f(1280, 16, 96, 192, 3) == 0
     assert f(4, 2, 16, 32, 0) == 1
+    assert f(4, 2, 16, 32, 1) == 1
     assert f(4, 2, 64, 192, 0) == 0
     assert f(0, 2, 96, 192, 0) == 0
 
@@ -379,12 +384,20 @@ def test_fused_entry_points_reject_bad_arguments(lib):
     dv_ = T(0x300000, sb=2 * 192, sh=192)
     dout = T(0x400000, sb=2 * 192, sh=192)
     dg = T(0x500000, sb=2 * 192, sh=192)
-    dec = lambda gg=dg, aug=0xA000, y=dout: lib.gla_decode_step_fused(
+    dec = lambda gg=dg, aug=0xA000, y=dout, ws=None, nws=0: lib.gla_decode_step_fused(
         4, 2, 96, 192, ref(dq), ref(dk_), ref(dv_), 0x9000, 0xC00000, 2 * 96 * 192, ref(gg) if gg else None,
-        aug, 0xB000, ctypes.c_float(1e-6), ref(y), None)
+        aug, 0xB000, ctypes.c_float(1e-6), ref(y), ws, nws, None)
     assert dec(gg=None) == NULL
     assert dec(aug=None) == NULL
     assert dec(y=T(0x500000, sb=2 * 192, sh=192)) == ALIAS
+    # the optional workspace: o' and the slices' sums of squares
+    need = lib.gla_decode_step_fused_workspace(4, 2, 96, 192)
+    assert need == 4 * 2 * (192 + 4) * 4
+    assert lib.gla_decode_step_fused_workspace(4, 2, 16, 32) == 0  # one workgroup per state
+    assert lib.gla_decode_step_fused_workspace(0, 2, 96, 192) == 0
+    assert dec(ws=0xE00000, nws=need - 4) == WS
+    assert dec(ws=0xE00008, nws=need) == WS
+    assert dec(ws=0x500000, nws=need) == ALIAS  # the gate stream
 
 
 # ------------------------------------------------------------ launch-size limits

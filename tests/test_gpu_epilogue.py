@@ -99,12 +99,15 @@ def test_fused_training_shape_sampled(gla):
         assert ey <= TOL["bf16"] and eS <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("dims", [(16, 32, "f32"), (96, 192, "bf16"), (96, 192, "f32")])
-def test_fused_decode_steps(gla, dims):
+def test_fused_decode_steps(gla, dims, use_ws):
     """The decode step with the epilogue against oracle.decode_step followed
-    by oracle.epilogue, over several steps (state updated in place)."""
+    by oracle.epilogue, over several steps (state updated in place), with the
+    workspace (column slices + normalisation kernel at (96, 192)) and
+    without (one workgroup per state)."""
     dk, dv, dtype = dims
-    flush(f"test_fused_decode_steps dk={dk} dv={dv} {dtype}")
+    flush(f"test_fused_decode_steps dk={dk} dv={dv} {dtype} workspace={use_ws}")
     N, H, steps = 29, 3, 4
     x = inputs.random_chunk_inputs(760 + dk, N, H, steps, dk, dv, dtype=dtype, scale=1.0)
     e = inputs.epilogue_inputs(760 + dk, N, H, steps, dk, dv, dtype, aug_scale=0.2)
@@ -114,7 +117,8 @@ def test_fused_decode_steps(gla, dims):
     for t in range(steps):
         q, k, v, g = (dev(np.ascontiguousarray(arr[:, :, t]), dtype)
                       for arr in (x["q"], x["k"], x["v"], e["g"]))
-        y = gla.decode_step_fused_(q, k, v, lam, S, g, aug, gam, EPS, out_dtype=torch.float32)
+        y = gla.decode_step_fused_(q, k, v, lam, S, g, aug, gam, EPS, out_dtype=torch.float32,
+                                   use_workspace=use_ws)
         ro, Sref = oracle.decode_step(x["q"][:, :, t], x["k"][:, :, t], x["v"][:, :, t], x["lam"], Sref)
         sl = lambda a: a[:, :, t:t + 1]
         ry = oracle.epilogue(sl(x["q"]), sl(x["k"]), sl(x["v"]), ro[:, :, None], e["aug"], e["gamma"], EPS,
@@ -133,7 +137,9 @@ def test_fused_decode_full_slab_sampled(gla):
     for bit, the bf16 output must be the fp32 output rounded to nearest
     (within one bf16 ulp), and for 12 sampled (sequence, head) pairs the fp32
     output and the state must match oracle.decode_step + oracle.epilogue to
-    1e-5."""
+    1e-5.  The step runs with its workspace, as benchmarked; the same step
+    without a workspace (one workgroup per state) on a third copy must give
+    the same state and an fp32 output within 1e-5 of it."""
     flush("test_fused_decode_full_slab_sampled N=1280 H=16")
     N, H, dk, dv, steps = 1280, 16, 96, 192, 2
     g = torch.Generator(device="cuda")
@@ -154,13 +160,16 @@ def test_fused_decode_full_slab_sampled(gla):
     for st in range(steps):
         blk, gs = qkv[st], gz[st]
         qv, kv, vv = blk[..., :dk], blk[..., dk:2 * dk], blk[..., 2 * dk:]
-        S32, Spl = S.clone(), S.clone()
+        S32, Spl, Snw = S.clone(), S.clone(), S.clone()
         gla.decode_step_fused_(qv, kv, vv, lam, S, gs, aug, gam, EPS, y=y16)
         y32 = gla.decode_step_fused_(qv, kv, vv, lam, S32, gs, aug, gam, EPS, out_dtype=torch.float32)
         gla.decode_step_(qv, kv, vv, lam, Spl, out_dtype=torch.float32)
+        ynw = gla.decode_step_fused_(qv, kv, vv, lam, Snw, gs, aug, gam, EPS, out_dtype=torch.float32,
+                                     use_workspace=False)
         torch.cuda.synchronize()
-        assert torch.equal(S, S32) and torch.equal(S, Spl), st
-        del S32, Spl
+        assert torch.equal(S, S32) and torch.equal(S, Spl) and torch.equal(S, Snw), st
+        assert oracle.rel_err(host(ynw), host(y32)) <= 1e-5, st
+        del S32, Spl, Snw, ynw
         a = y16.view(torch.int16).cpu().numpy().astype(np.int32)
         b = y32.to(torch.bfloat16).view(torch.int16).cpu().numpy().astype(np.int32)
         assert np.max(np.abs(a - b)) <= 1, st
