@@ -320,18 +320,20 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     return dict(bytes=nbytes, reps=reps)
 
 
-# the sources that decide the chunked backward's kernels and launches
+# the sources that decide the chunked kernels and their launches, and those
+# of the decode step
 CHUNK_SOURCES = ("gla_api.cpp", "gla_chunk.hip", "gla_common.hpp", "gla_internal.h")
+DECODE_SOURCES = ("gla_api.cpp", "gla_decode.hip", "gla_common.hpp", "gla_internal.h")
 
 
-def kernel_source_digest():
-    """sha256 over the chunked kernels' sources; traffic figures are only
-    valid for the sources they were counted on."""
+def kernel_source_digest(names=CHUNK_SOURCES):
+    """sha256 over kernel sources; counted figures are only valid for the
+    sources they were counted on."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(REPO, "gated_linear_attention_gla_amd", "csrc")
-    for name in CHUNK_SOURCES:
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -351,6 +353,23 @@ def counted_traffic():
     if t.get("kernel_source_sha256") != kernel_source_digest():
         return None
     return t.get("bwd_call_bytes")
+
+
+DECODE_TRAFFIC_FILE = os.path.join(REPO, "profiles", "decode_and_conv_kernels_traffic.json")
+
+
+def counted_decode_traffic():
+    """HBM bytes per decode layer call (1,280 x 16 states) from the committed
+    counter summary, or None when it is missing or was counted on other
+    decode sources."""
+    try:
+        with open(DECODE_TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest(DECODE_SOURCES):
+        return None
+    return t.get("decode_call_bytes")
 
 
 MFMA_FILE = os.path.join(REPO, "profiles", "chunk_kernels_training_mfma_lds.json")
@@ -686,7 +705,9 @@ def main():
     }
     if dec is not None:
         out["decode_roofline"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": dec["hbm_frac"]}
+                                  "unit": "GB/s", "frac": dec["hbm_frac"], "traffic": counted_decode_traffic(),
+                                  "bytes_per_launch": DEC_BYTES * 1280 * 16,
+                                  "ms_per_launch": dec["ms_per_layer_call"]}
     print(json.dumps(out), flush=True)
 
 
