@@ -186,3 +186,31 @@ def test_fused_decode_full_slab_sampled(gla):
             assert oracle.rel_err(got[n, h], ry[0, 0, 0]) <= 1e-5, (st, n, h)
     for n, h in pairs:
         assert oracle.rel_err(host(S[n, h]), ref_S[(n, h)]) <= 1e-5, (n, h)
+
+
+def test_fused_decode_single_state_bf16_out(gla):
+    """One sequence and one head (N * H = 1) with bf16 inputs and output: the
+    workspace path (column slices + normalisation kernel) against the oracle,
+    with the bf16 output equal to the fp32 output rounded to nearest (within
+    one bf16 ulp), and the same state as the path without a workspace."""
+    flush("test_fused_decode_single_state_bf16_out")
+    dk, dv = 96, 192
+    x = inputs.random_chunk_inputs(790, 1, 1, 1, dk, dv, dtype="bf16", scale=1.0)
+    e = inputs.epilogue_inputs(790, 1, 1, 1, dk, dv, "bf16", aug_scale=0.2)
+    S_host = inputs.normal(790, inputs.TID["S"], (1, 1, dk, dv), 0.01, "f32")
+    q, k, v, g = (dev(np.ascontiguousarray(arr[:, :, 0]), "bf16") for arr in (x["q"], x["k"], x["v"], e["g"]))
+    lam, aug, gam = dev_f32(x["lam"]), dev_f32(e["aug"]), dev_f32(e["gamma"])
+    S16, S32, Snw = dev_f32(S_host), dev_f32(S_host), dev_f32(S_host)
+    y16 = gla.decode_step_fused_(q, k, v, lam, S16, g, aug, gam, EPS, out_dtype=torch.bfloat16)
+    y32 = gla.decode_step_fused_(q, k, v, lam, S32, g, aug, gam, EPS, out_dtype=torch.float32)
+    gla.decode_step_fused_(q, k, v, lam, Snw, g, aug, gam, EPS, out_dtype=torch.float32, use_workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(S16, S32) and torch.equal(S16, Snw)
+    a = y16.view(torch.int16).cpu().numpy().astype(np.int32)
+    b = y32.to(torch.bfloat16).view(torch.int16).cpu().numpy().astype(np.int32)
+    assert np.max(np.abs(a - b)) <= 1
+    ro, rS = oracle.decode_step(x["q"][:, :, 0], x["k"][:, :, 0], x["v"][:, :, 0], x["lam"], S_host)
+    ry = oracle.epilogue(x["q"], x["k"], x["v"], ro[:, :, None], e["aug"], e["gamma"], EPS, e["g"])[:, :, 0]
+    assert oracle.rel_err(host(y32), ry) <= 1e-5
+    assert oracle.rel_err(host(S32), rS) <= 1e-5
+

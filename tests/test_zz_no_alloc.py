@@ -41,3 +41,26 @@ def test_noalloc_matches_workspace_entry_point(gla):
         eo, eS = oracle.rel_err(host(o), ro), oracle.rel_err(host(S_T), rS)
         flush(f"  equal to gla_chunk_fwd; oracle err o={eo:.3e} S_T={eS:.3e}")
         assert eo <= TOL["bf16"] and eS <= TOL["bf16"]
+
+
+def test_noalloc_without_segment_split_and_empty(gla):
+    """Dims that need no segment states (the training batch size, and an
+    empty sequence) take no scratch at all: results equal gla_chunk_fwd's;
+    T = 0 passes S0 through as S_T."""
+    lib = gla.load_library()
+    for seed, B, H, T, chunk in ((603, 8, 16, 256, 64), (604, 1, 2, 0, 64)):
+        flush(f"test_noalloc_without_segment_split_and_empty B={B} H={H} T={T}")
+        x = inputs.random_chunk_inputs(seed, B, H, T, 96, 192, dtype="bf16")
+        d = gla.GlaDims(B, H, T, 96, 192, chunk)
+        assert lib.gla_chunk_fwd_workspace(ctypes.byref(d)) == 0
+        q, k, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
+        lam, S0 = dev_f32(x["lam"]), dev_f32(x["S0"])
+        o = torch.empty((B, H, T, 192), dtype=torch.bfloat16, device="cuda")
+        S_T = torch.empty((B, H, 96, 192), dtype=torch.float32, device="cuda")
+        gla.chunk_fwd_noalloc(q, k, v, lam, S0, o, S_T, chunk=chunk)
+        o_ref, S_ref = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S_T, S_ref)
+        if T == 0:
+            assert torch.equal(S_T, S0)
+
