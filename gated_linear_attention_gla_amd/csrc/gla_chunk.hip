@@ -505,17 +505,11 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 
   // writes 4 consecutive masked-P values of row i (cols 16 J + 4 g ..) as NTP planes
   auto put_p = [&](int i, int J, const f32x4& val) {
+    const float x[4] = {val[0], val[1], val[2], val[3]};
+    bf16x4 pk[NTP];
+    split_vec<NTP>(x, pk);
 #pragma unroll
-    for (int p = 0; p < NTP; ++p) {
-      bf16x4 pk;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        __bf16 t[NTP];
-        split_terms<NTP>(val[r], t);
-        pk[r] = t[p];
-      }
-      *reinterpret_cast<bf16x4*>(&sP[p * CP * PP + i * PP + 16 * J + 4 * g]) = pk;
-    }
+    for (int p = 0; p < NTP; ++p) *reinterpret_cast<bf16x4*>(&sP[p * CP * PP + i * PP + 16 * J + 4 * g]) = pk[p];
   };
   // zero tiles read by the 32-deep k-steps of stage 3: forward (I, I+1) for
   // even I, reverse (I, I-1) for odd I
@@ -713,16 +707,15 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       const int ks = rh * KSDO + kso;
       bf16x8 Sf[NS][NTS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s) {
+        float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int Do = 2 * kso + (e >> 2);
-          const float x = (Do < DKTO) ? accS[Do < DKTO ? Do : 0][s][e & 3] : 0.0f;
-          __bf16 t[NTS];
-          split_terms<NTS>(x, t);
-#pragma unroll
-          for (int p = 0; p < NTS; ++p) Sf[s][p][e] = t[p];
+          x[e] = (Do < DKTO) ? accS[Do < DKTO ? Do : 0][s][e & 3] : 0.0f;
         }
+        split_vec<NTS>(x, Sf[s]);
+      }
 #pragma unroll
       for (int I = 0; I < CT; ++I) {
         bf16x8 Aq[NT];
@@ -881,17 +874,17 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         const f32x4 cf1 = *reinterpret_cast<const f32x4*>(&sColF[32 * ks + 8 * g + 4]);
         const float cf[8] = {cf0[0], cf0[1], cf0[2], cf0[3], cf1[0], cf1[1], cf1[2], cf1[3]};
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS; ++s) {
+          float x[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float x = 0.0f;
+            float v = 0.0f;
 #pragma unroll
-            for (int p = 0; p < NT; ++p) x += bf16v_to_f32(Bv[s][p][e]);
-            __bf16 t[NTK];
-            split_terms<NTK>(x * cf[e], t);
-#pragma unroll
-            for (int p = 0; p < NTK; ++p) Bs[s][p][e] = t[p];
+            for (int p = 0; p < NT; ++p) v += bf16v_to_f32(Bv[s][p][e]);
+            x[e] = v * cf[e];
           }
+          split_vec<NTK>(x, Bs[s]);
+        }
       }
 #pragma unroll
       for (int Do = 0; Do < DKTO; ++Do) {

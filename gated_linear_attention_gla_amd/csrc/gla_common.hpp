@@ -51,6 +51,41 @@ __device__ __forceinline__ void split_terms(float x, __bf16 (&t)[NT]) {
   }
 }
 
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two-term split of a pair: hi = RNE(x), lo = RNE(x - hi), each pair packed
+// with element 0 in the low half.  One packed conversion yields both hi
+// values, and their fp32 values are the packed word shifted or masked, so a
+// pair costs six VALU instructions (the same terms as split_terms<2>).
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){x0, x1}, bf16x2v));
+  const float r0 = x0 - __uint_as_float(u << 16);
+  const float r1 = x1 - __uint_as_float(u & 0xffff0000u);
+  hi = u;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){r0, r1}, bf16x2v));
+}
+
+// x[0..N) -> NT bf16 term vectors t[p] (N = 4 or 8), pairwise for two terms.
+template <int NT, int N, typename V>
+__device__ __forceinline__ void split_vec(const float (&x)[N], V (&t)[NT]) {
+  if constexpr (NT == 2) {
+    uint32_t h[N / 2], l[N / 2];
+#pragma unroll
+    for (int p = 0; p < N / 2; ++p) split_pair(x[2 * p], x[2 * p + 1], h[p], l[p]);
+    t[0] = __builtin_bit_cast(V, h);
+    t[1] = __builtin_bit_cast(V, l);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      __bf16 s[NT];
+      split_terms<NT>(x[e], s);
+#pragma unroll
+      for (int p = 0; p < NT; ++p) t[p][e] = s[p];
+    }
+  }
+}
+
 // c += A * B over all term pairs (ia, ib) with ia + ib < max(NA, NB): the
 // products dropped are below the precision the longer operand carries.
 template <int NA, int NB>
