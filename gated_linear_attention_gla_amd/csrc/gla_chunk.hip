@@ -445,9 +445,14 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     const int d = rev ? (4 * g + r - li) : (li - 4 * g - r);
     dmask[r] = d >= 0 ? lam_pow_f32(lam, d) : 0.0f;
   }
-  // off-diagonal P-tile factors lam^(16 + e), e = li - 4 g - r (reverse:
-  // 4 g + r - li), e in [-15, 15]; read from the table once it is complete
+  // Off-diagonal P-tile factors: the exponent of tile distance d = Ip - Jp
+  // >= 1 is 16 d + e with e = li - 4 g - r (reverse: 4 g + r - li), formed
+  // as lam^(16 (d - 1)) times lp[r] = lam^(16 + e).  Where a wave has at
+  // most two tile slots (slot kt holds the same tile in every chunk) their
+  // whole factors are kept in mf instead, filled once the table is complete.
+  constexpr bool MFT = !TIGHT && MAXPT <= 2 && NT == 1;
   float lp[4] = {0.f, 0.f, 0.f, 0.f};
+  float mf[MFT ? MAXPT : 1][4] = {};
 
   const char* qb = reinterpret_cast<const char*>(a.q);
   const char* kb = reinterpret_cast<const char*>(a.k);
@@ -601,6 +606,18 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 #pragma unroll
       for (int r = 0; r < 4; ++r) lp[r] = sPow[16 + (rev ? 4 * g + r - li : li - 4 * g - r)];
     }
+    if constexpr (MFT) {
+#pragma unroll
+      for (int kt = 0; kt < MAXPT; ++kt) {
+        const int t = w + kt * NW;
+        int Ip, Jp;
+        tile_of<CT>(t < NPT ? t : 0, Ip, Jp);
+        const int d = Ip - Jp;
+        const float s16 = sPow[16 * (d > 0 ? d - 1 : 0)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mf[kt][r] = d == 0 ? dmask[r] : s16 * lp[r];
+      }
+    }
   }
 
   for (int64_t ci = 0; ci < nchunks; ++ci) {
@@ -654,16 +671,17 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         }
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-          // acc[r] = q'_i . k'_j with i = 16 I + li, j = 16 J + 4 g + r.  The
-          // diagonal tile takes the per-lane mask; off the diagonal the
-          // exponent is 16 d + base -/+ r (d = Ip - Jp >= 1), formed as
-          // lam^(16 (d - 1)) (one value per tile) times lp[r] = lam^(16 + base -/+ r).
-          // (register-tight shapes read the whole exponent from the table)
+          // acc[r] = q'_i . k'_j with i = 16 I + li, j = 16 J + 4 g + r, times
+          // its decay mask (register-tight shapes read the whole exponent
+          // 16 d + base -/+ r from the table)
           if constexpr (TIGHT) {
             const int base = 16 * da[u] + (rev ? 4 * g - li : li - 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               acc[u][r] *= da[u] == 0 ? dmask[r] : sPow[da[u] == 0 ? 0 : (rev ? base + r : base - r)];
+          } else if constexpr (MFT) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[u][r] *= mf[kt0 + u][r];
           } else {
             const float s16 = sPow[16 * (da[u] > 0 ? da[u] - 1 : 0)];
 #pragma unroll
@@ -878,9 +896,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           float x[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float v = 0.0f;
+            float v = bf16v_to_f32(Bv[s][0][e]);
 #pragma unroll
-            for (int p = 0; p < NT; ++p) v += bf16v_to_f32(Bv[s][p][e]);
+            for (int p = 1; p < NT; ++p) v += bf16v_to_f32(Bv[s][p][e]);
             x[e] = v * cf[e];
           }
           split_vec<NTK>(x, Bs[s]);
