@@ -439,12 +439,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   };
   // decay mask of the diagonal P tiles, per lane: forward keeps j <= i with
   // lam^(i-j), reverse keeps j >= i with lam^(j-i); i = 16 I + li, j = 16 I + 4 g + r
-  float dmask[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int d = rev ? (4 * g + r - li) : (li - 4 * g - r);
-    dmask[r] = d >= 0 ? lam_pow_f32(lam, d) : 0.0f;
-  }
+  // (read from the table once it is complete)
+  float dmask[4] = {0.f, 0.f, 0.f, 0.f};
   // Off-diagonal P-tile factors: the exponent of tile distance d = Ip - Jp
   // >= 1 is 16 d + e with e = li - 4 g - r (reverse: 4 g + r - li), formed
   // as lam^(16 (d - 1)) times lp[r] = lam^(16 + e).  Where a wave has at
@@ -483,13 +479,17 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         }
   }
   // The segments before this one (in walk order) enter through their end
-  // states: S <- lam^len S + E, oldest first.
+  // states: S <- lam^len S + E, oldest first.  Every such segment is whole
+  // except, in reverse time, the last one (walked first), so two powers
+  // serve them all.
   if constexpr (!SO) {
     const int first = REV ? nseg - 1 : 0;
     const int step = REV ? -1 : 1;
+    const int64_t tail = T - (int64_t)(nseg - 1) * a.seg_len;  // the last segment's length
+    const float dec_full = first != seg ? lam_pow_f32(lam, (int)a.seg_len) : 1.0f;
+    const float dec_last = (REV && first != seg) ? lam_pow_f32(lam, (int)tail) : dec_full;
     for (int p = first; p != seg; p += step) {
-      const int64_t len = (T - p * a.seg_len) < a.seg_len ? (T - p * a.seg_len) : a.seg_len;
-      const float dec = lam_pow_f32(a.lam[h], (int)len);
+      const float dec = p == nseg - 1 ? dec_last : dec_full;
       const float* E = a.seg_state + (bh * nseg + p) * (int64_t)DK * DV;
 #pragma unroll
       for (int Do = 0; Do < DKTO; ++Do)
@@ -602,6 +602,13 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     pfv.store(sV, tid);
     __syncthreads();  // sPow complete
     fill_factors(chunk_len(chunk_start(0)));
+    if constexpr (!SO) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = rev ? (4 * g + r - li) : (li - 4 * g - r);
+        dmask[r] = d >= 0 ? sPow[d] : 0.0f;
+      }
+    }
     if constexpr (!TIGHT) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) lp[r] = sPow[16 + (rev ? 4 * g + r - li : li - 4 * g - r)];
