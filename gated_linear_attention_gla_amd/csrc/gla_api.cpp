@@ -481,7 +481,7 @@ gla_status gla_conv1d_fwd(int64_t B, int64_t T, int64_t D, const gla_tensor* x, 
   if (!x || !w || !y) return GLA_ERR_NULL;
   if (B < 1 || T < 0 || !conv_dims_ok(D) || B > ((int64_t)1 << 24) || T > ((int64_t)1 << 40))
     return GLA_ERR_SHAPE;
-  if (gla::conv_fwd_blocks(B, T, D) > (int64_t)0xFFFFFFFF / gla::conv_block_threads()) return GLA_ERR_SHAPE;
+  if (gla::conv_fwd_blocks(B, T, D) > (int64_t)0xFFFFFFFF / gla::conv_fwd_threads()) return GLA_ERR_SHAPE;
   gla_status st;
   if (T > 0) {
     if ((st = check_act(x, B, T, D)) != GLA_OK) return st;

@@ -23,7 +23,9 @@ namespace {
 
 constexpr int CW = 4;        // convolution width
 constexpr int CT = 16;       // tokens per thread run
-constexpr int CTHR = 64;     // threads per workgroup (512 channels)
+constexpr int CTHR = 64;     // threads per wave (512 channels)
+constexpr int RW = 4;        // prefill: waves per workgroup, one run each
+static_assert(8 % RW == 0, "the tap staging splits 8 vectors per lane over the waves");
 
 // 8 stored input values held between the load and their use (raw, so a bf16
 // row costs 4 registers while its load is in flight)
@@ -111,30 +113,42 @@ __device__ __forceinline__ void load_taps(const f32x4* w4, const float* bias, in
 
 // one thread = 8 channels x one run of CT tokens of one sequence
 template <bool IN_F32, bool OUT_F32>
-__global__ void __launch_bounds__(CTHR) conv_fwd_kernel(ConvArgs a) {
-  // block id = (b * runs + run) * channel blocks + channel block
+__global__ void __launch_bounds__(CTHR * RW) conv_fwd_kernel(ConvArgs a) {
+  // Work items (sequence, channel block, group of RW consecutive runs), run
+  // groups fastest, are dealt to the 8 XCDs in contiguous ranges: block ids
+  // congruent mod 8 share an XCD, so the 3 window rows a run reads before its
+  // first token were just read by the neighbouring run (another wave of the
+  // workgroup, or the previous workgroup on the XCD) and come from L2.
   const int64_t cblocks = (a.D / 8 + CTHR - 1) / CTHR;
   const int64_t runs = a.T > 0 ? (a.T + CT - 1) / CT : 1;
+  const int64_t rgroups = (runs + RW - 1) / RW;
+  const int64_t items = a.B * rgroups * cblocks;
+  const int64_t per_xcd = (items + 7) / 8;
   const int64_t bid = blockIdx.x;
-  const int64_t cb = bid % cblocks;
-  const int64_t run = (bid / cblocks) % runs;
-  const int64_t b = bid / (cblocks * runs);
-  const int64_t c0 = (cb * CTHR + threadIdx.x) * 8;
-  // The block's taps are staged in LDS with coalesced loads: read directly,
-  // each lane's 128 contiguous bytes make every load instruction touch 64
-  // cache lines.  Every thread takes part, also those past the last channel.
+  const int64_t item = (bid & 7) * per_xcd + (bid >> 3);
+  if (item >= items) return;  // the padding of the last XCD's range (whole workgroup)
+  const int tx = (int)threadIdx.x % CTHR;
+  const int wr = (int)threadIdx.x / CTHR;  // this wave's run in the group
+  const int64_t run = (item % rgroups) * RW + wr;
+  const int64_t cb = (item / rgroups) % cblocks;
+  const int64_t b = item / (rgroups * cblocks);
+  const int64_t c0 = (cb * CTHR + tx) * 8;
+  // The block's taps are staged in LDS once for its RW runs, with coalesced
+  // loads: read directly, each lane's 128 contiguous bytes make every load
+  // instruction touch 64 cache lines.  Every thread takes part, also those
+  // past the last channel or run.
   __shared__ f32x4 sw[CTHR * 8];
   {
     const int64_t cbase = cb * CTHR * 8;
     const f32x4* wsrc = reinterpret_cast<const f32x4*>(a.w) + cbase;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = k * CTHR + (int)threadIdx.x;
+    for (int k = 0; k < 8 / RW; ++k) {
+      const int i = k * CTHR * RW + (int)threadIdx.x;
       if (cbase + i < a.D) sw[i] = wsrc[i];
     }
   }
   __syncthreads();
-  if (c0 >= a.D) return;
+  if (c0 >= a.D || run >= runs) return;
   const int64_t t0 = run * CT;
   const int64_t t1 = (a.T - t0) < CT ? a.T : t0 + CT;
   float wt[CW][8], bs[8];
@@ -173,7 +187,7 @@ __global__ void __launch_bounds__(CTHR) conv_fwd_kernel(ConvArgs a) {
     }
   };
   load_group(0, xr[0]);
-  load_taps(sw + threadIdx.x * 8, a.bias, c0, wt, bs);
+  load_taps(sw + tx * 8, a.bias, c0, wt, bs);
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     if (gi + 1 < G) load_group(gi + 1, xr[(gi + 1) & 1]);
@@ -274,14 +288,15 @@ __global__ void __launch_bounds__(CTHR) conv_step_kernel(ConvStepArgs a) {
 
 int64_t conv_fwd_blocks(int64_t B, int64_t T, int64_t D) {
   const int64_t runs = T > 0 ? (T + CT - 1) / CT : 1;
-  return B * runs * ((D / 8 + CTHR - 1) / CTHR);
+  return (B * ((runs + RW - 1) / RW) * ((D / 8 + CTHR - 1) / CTHR) + 7) / 8 * 8;
 }
+int conv_fwd_threads() { return CTHR * RW; }
 
 int64_t conv_step_blocks(int64_t N, int64_t D) { return (N + SQ - 1) / SQ * ((D / 8 + CTHR - 1) / CTHR); }
 int conv_block_threads() { return CTHR; }
 
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)conv_fwd_blocks(a.B, a.T, a.D)), block(CTHR);
+  const dim3 grid((unsigned)conv_fwd_blocks(a.B, a.T, a.D)), block(CTHR * RW);
   if (a.in_f32) {
     if (a.out_f32) hipLaunchKernelGGL((conv_fwd_kernel<true, true>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((conv_fwd_kernel<true, false>), grid, block, 0, st, a);

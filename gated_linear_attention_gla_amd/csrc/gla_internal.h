@@ -142,9 +142,10 @@ int decode_slices(int64_t states, int dk, int dv, bool epi, bool has_ws);
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);
 hipError_t launch_conv_step(const ConvStepArgs& a, hipStream_t st);
 // one-dimensional grid sizes of the two convolution launches, and their
-// workgroup size
+// workgroup sizes (decode step, prefill)
 int64_t conv_fwd_blocks(int64_t B, int64_t T, int64_t D);
 int64_t conv_step_blocks(int64_t N, int64_t D);
 int conv_block_threads();
+int conv_fwd_threads();
 
 }  // namespace gla
