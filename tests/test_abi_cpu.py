@@ -419,8 +419,8 @@ def test_launch_size_limits(lib):
     to = gb.GlaTensor(0x400000, gb.GLA_BF16, 0, 192, 1024 * 192)
     assert lib.gla_chunk_fwd_varlen((1 << 11) + 1, 1024, 100, 96, 192, 64, ref(tq), ref(tk), ref(tv), 0x700000,
                                     0x9000, 0x800000, 8, 1024 * 96 * 192, None, None, ref(to), None) == SHAPE
-    # convolution: 2^16 sequences of 2^16 tokens, 64 channels: 2^28 workgroups
-    # (fewer than 2^32) but more than 2^32 work-items
+    # convolution: 2^16 sequences of 2^16 tokens, 64 channels: 2^26
+    # workgroups of 4 waves (fewer than 2^32) but 2^34 work-items
     x, y = act(0x100000), act(0x200000)
     assert conv_fwd(lib, 1 << 16, 1 << 16, 64, x, y) == SHAPE
     # conv decode step: 2^24 sequences of 2^15 channels: 2^30 workgroups
