@@ -11,7 +11,7 @@ library must be built in-tree first (python -m gated_linear_attention_gla_amd.bu
 __all__ = [
     "chunk_fwd", "chunk_bwd", "decode_step_",
     "chunk_fwd_fused", "decode_step_fused_", "chunk_fwd_varlen",
-    "conv1d_fwd", "conv1d_step_",
+    "conv1d_fwd", "conv1d_step_", "set_segment_wait",
     "load_library", "GlaError",
 ]
 

@@ -80,6 +80,8 @@ def load_library(path=LIB_PATH):
     lib.gla_chunk_fwd_workspace.argtypes = [P(GlaDims)]
     lib.gla_chunk_bwd_workspace.restype = ctypes.c_size_t
     lib.gla_chunk_bwd_workspace.argtypes = [P(GlaDims)]
+    lib.gla_set_segment_wait.restype = None
+    lib.gla_set_segment_wait.argtypes = [ctypes.c_int32]
     lib.gla_chunk_fwd.restype = ctypes.c_int
     lib.gla_chunk_fwd.argtypes = [
         P(GlaDims), P(GlaTensor), P(GlaTensor), P(GlaTensor), vp, vp,
@@ -206,6 +208,13 @@ def _same_device(*tensors):
 
 def _state_ok(S, B, H, dk, dv, name):
     _expect(S, (B, H, dk, dv), name, torch.float32, contiguous=True)
+
+
+def set_segment_wait(microseconds):
+    """Bound on how long a workgroup of the one-launch segment split waits for
+    an earlier segment's end state before forming it itself (negative: the
+    default; 0: form every unpublished state at once).  Speed only."""
+    load_library().gla_set_segment_wait(int(microseconds))
 
 
 def chunk_fwd(q, k, v, lam, S0=None, chunk=64, out_dtype=None, o=None, S_T=None,

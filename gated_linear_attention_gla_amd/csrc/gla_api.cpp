@@ -27,7 +27,10 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <chrono>
 #include <mutex>
+#include <random>
 
 // Device scratch of gla_chunk_fwd_noalloc: the segment end states of its
 // segment split (the same use as gla_chunk_fwd's workspace).  Every GPU the
@@ -92,6 +95,40 @@ size_t pass_workspace(const gla_dims* d, int dk, int dv) {
   const int nseg = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk);
   if (nseg <= 1) return 0;
   return (size_t)d->B * d->H * nseg * d->dk * d->dv * sizeof(float);
+}
+
+// Flags of a one-launch segment split: one 8-byte word per (b, h, column
+// block, segment), with at most dv / 16 column blocks.
+size_t seg_flag_bytes(const gla_dims* d, int dv) {
+  const int nseg = gla::chunk_segments(d->B, d->H, d->T, (int)d->dk, dv, (int)d->chunk);
+  if (nseg <= 1) return 0;
+  return (size_t)d->B * d->H * nseg * ((dv + 15) / 16) * sizeof(unsigned long long);
+}
+
+// Tag of one call's segment flags: a nonzero 56-bit epoch, distinct per call
+// in this process and seeded per process, above the 8 bits that carry the
+// XCD id.  Flags left by other calls, processes or earlier users of the
+// memory never carry it.
+std::atomic<uint64_t> g_seg_epoch{0};
+uint64_t next_seg_tag() {
+  static const uint64_t seed = [] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (((uint64_t)rd() << 32) ^ rd() ^ (t * 0x9E3779B97F4A7C15ull));
+  }();
+  uint64_t e = (seed + g_seg_epoch.fetch_add(1, std::memory_order_relaxed)) & ((1ull << 56) - 1);
+  if (e == 0) e = 1;
+  return e << 8;
+}
+
+// Bound on a workgroup's wait for the earlier segments' states, in ticks of
+// the 100 MHz clock: by default 20 us plus 4 us per chunk of a segment (about
+// four times a state pass), or the fixed bound set by gla_set_segment_wait.
+std::atomic<int32_t> g_seg_wait_us{-1};
+uint32_t seg_wait_ticks(int64_t seg_chunks) {
+  const int32_t us = g_seg_wait_us.load(std::memory_order_relaxed);
+  const int64_t t = us >= 0 ? (int64_t)us * 100 : 2000 + 400 * seg_chunks;
+  return (uint32_t)(t > 0xffffffffll ? 0xffffffffll : t);
 }
 
 void set_segments(ChunkArgs& a, const gla_dims* d, int dk, int dv, void* ws) {
@@ -178,7 +215,11 @@ const char* gla_status_string(gla_status s) {
 
 size_t gla_chunk_fwd_workspace(const gla_dims* dims) {
   if (!dims || check_dims(dims) != GLA_OK) return 0;
-  return pass_workspace(dims, (int)dims->dk, (int)dims->dv);
+  return pass_workspace(dims, (int)dims->dk, (int)dims->dv) + seg_flag_bytes(dims, (int)dims->dv);
+}
+
+void gla_set_segment_wait(int32_t microseconds) {
+  g_seg_wait_us.store(microseconds < 0 ? -1 : microseconds, std::memory_order_relaxed);
 }
 
 size_t gla_chunk_bwd_workspace(const gla_dims* dims) {
@@ -577,6 +618,12 @@ gla_status chunk_fwd_impl(const gla_dims* dims, const gla_tensor* q, const gla_t
 
   ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, o, 0);
   set_segments(a, dims, (int)dims->dk, (int)dims->dv, ws);
+  if (a.nseg > 1) {  // one launch: the flags follow the segment states
+    a.seg_flag = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
+                                                       pass_workspace(dims, (int)dims->dk, (int)dims->dv));
+    a.seg_tag = next_seg_tag();
+    a.seg_wait = seg_wait_ticks(a.seg_len / C);
+  }
   if (gla::launch_chunk_pass((int)dims->dk, (int)dims->dv, (int)dims->chunk, a, s) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;

@@ -31,6 +31,9 @@
 #include "gla_common.hpp"
 #include "gla_internal.h"
 
+// cache policy of a buffer access: sc1 (device scope)
+constexpr int kCpolSc1 = 16;
+
 namespace gla {
 
 // lam^n for n >= 0 in fp32, computed in double; 0^0 = 1.
@@ -262,8 +265,10 @@ struct ChunkLds {
 // One chunk pass for workgroup slot xb of a launch (the whole body of the
 // kernels below).  SO (state only): the segment state pass -- only the state
 // update runs, from a zero state, and the segment's end state goes to
-// a.seg_state.
-template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false, bool PACKED = false>
+// a.seg_state.  MRG: the earlier segments' states were written in this same
+// launch, by other workgroups on this XCD, and are read from L2.
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false, bool PACKED = false,
+          bool MRG = false>
 __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, char* const smem) {
   using Lds = ChunkLds<DK, BN, C, NT, NW, EPI>;
   constexpr int NTHR = NW * 64;
@@ -459,6 +464,13 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   const int64_t v_off = b * a.sv_b + h * a.sv_h + tbase * a.sv_t + (int64_t)nblk * BN;
   const int col0 = nblk * BN + ws * NS * 16 + li;  // + 16 s: this lane's column in strip s
 
+  // A segment's end state in the workspace, in the register order of the
+  // workgroups that write and read it (both run this tiling): per column
+  // block, 16-byte groups (a lane's four r values) indexed by (Do, s, thread).
+  auto seg_block = [&](int p) -> float* {
+    return a.seg_state + ((bh * nseg + p) * NBLK + nblk) * (int64_t)(DK * BN);
+  };
+
   // ---- state slice in accumulators: accS[Do][s][r] = S[state_row(D)][col0 + 16 s]
   // for this wave's row tiles D = rh DKTO + Do
   f32x4 accS[DKTO][NS];
@@ -488,17 +500,49 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     const int64_t tail = T - (int64_t)(nseg - 1) * a.seg_len;  // the last segment's length
     const float dec_full = first != seg ? lam_pow_f32(lam, (int)a.seg_len) : 1.0f;
     const float dec_last = (REV && first != seg) ? lam_pow_f32(lam, (int)tail) : dec_full;
-    for (int p = first; p != seg; p += step) {
-      const float dec = p == nseg - 1 ? dec_last : dec_full;
-      const float* E = a.seg_state + (bh * nseg + p) * (int64_t)DK * DV;
+    if constexpr (MRG && !REV) {
+      // States written in this launch by other workgroups: read at device
+      // scope (past this CU's cache), FB of them requested at once (all whole
+      // segments, so one power serves them), then folded in order.
+      constexpr int FB = TIGHT ? 1 : 4;
+      for (int p0 = 0; p0 < seg; p0 += FB) {
+        f32x4 e[FB][DKTO][NS];
 #pragma unroll
-      for (int Do = 0; Do < DKTO; ++Do)
+        for (int u = 0; u < FB; ++u) {
+          if (p0 + u >= seg) continue;
+          const __amdgpu_buffer_rsrc_t rs =
+              __builtin_amdgcn_make_buffer_rsrc(seg_block(p0 + u), (short)0, DK * BN * 4, 0x00020000);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+          for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            accS[Do][s][r] =
-                fmaf(dec, accS[Do][s][r], E[(int64_t)state_row<DK>(rh * DKTO + Do, g, r) * DV + col0 + 16 * s]);
+            for (int s = 0; s < NS; ++s)
+              e[u][Do][s] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((Do * NS + s) * NTHR + tid) * 16, 0, kCpolSc1));
+        }
+#pragma unroll
+        for (int u = 0; u < FB; ++u) {
+          if (p0 + u >= seg) continue;
+#pragma unroll
+          for (int Do = 0; Do < DKTO; ++Do)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) accS[Do][s][r] = fmaf(dec_full, accS[Do][s][r], e[u][Do][s][r]);
+        }
+      }
+    } else {
+      for (int p = first; p != seg; p += step) {
+        const float dec = p == nseg - 1 ? dec_last : dec_full;
+        const f32x4* const E = reinterpret_cast<const f32x4*>(seg_block(p));
+#pragma unroll
+        for (int Do = 0; Do < DKTO; ++Do)
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const f32x4 x = E[(Do * NS + s) * NTHR + tid];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accS[Do][s][r] = fmaf(dec, accS[Do][s][r], x[r]);
+          }
+      }
     }
   }
 
@@ -1136,20 +1180,22 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     }
   }
 
-  // the state pass hands its segment's end state to the later segments; the
-  // last segment in walk order returns the final state
-  float* dst = nullptr;
-  if constexpr (SO) dst = a.seg_state + (bh * nseg + seg) * (int64_t)DK * DV;
-  else if (s_final && seg == (REV ? 0 : nseg - 1)) dst = s_final;
-  if (dst) {
-    float* sf = dst;
+  // the state pass hands its segment's end state to the later segments (in
+  // register order); the last segment in walk order returns the final state
+  if constexpr (SO) {
+    f32x4* const E = reinterpret_cast<f32x4*>(seg_block(seg));
+#pragma unroll
+    for (int Do = 0; Do < DKTO; ++Do)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) E[(Do * NS + s) * NTHR + tid] = accS[Do][s];
+  } else if (s_final && seg == (REV ? 0 : nseg - 1)) {
 #pragma unroll
     for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          sf[(int64_t)state_row<DK>(rh * DKTO + Do, g, r) * DV + col0 + 16 * s] = accS[Do][s][r];
+          s_final[(int64_t)state_row<DK>(rh * DKTO + Do, g, r) * DV + col0 + 16 * s] = accS[Do][s][r];
   }
 }
 
@@ -1157,6 +1203,90 @@ template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool
 __global__ void __launch_bounds__(NW * 64) chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW, EPI>::BYTES];
   chunk_body<DK, DV, BN, NW, C, NT, REV, SO, EPI, PACKED>(a, blockIdx.x, smem);
+}
+
+// Hardware id of the XCD (its own L2) that runs this workgroup.
+__device__ __forceinline__ unsigned xcc_id() {
+  return __builtin_amdgcn_s_getreg(20 /* XCC_ID */ | (0 << 6) | ((4 - 1) << 11)) & 0xfu;
+}
+
+// A segment split in one launch.  Workgroup (unit, segment) first runs its
+// segment's state pass and publishes the end state (stores drained to L2,
+// then the flag); then one lane polls the flags of the segments before it in
+// walk order, which sit 8 (segment distance) workgroups earlier in dispatch
+// order and so -- workgroups being dealt to the XCDs in turn -- on the same
+// XCD, sharing its L2.  A flag counts only if it carries this call's tag and
+// this XCD's id.  Any earlier state not published within a.seg_wait ticks
+// (the producer not resident, or on another XCD) is formed here by the same
+// state pass, bit for bit what its producer writes.  Then the full pass folds
+// them in as in the two-launch form.  Every wait is bounded, so the launch
+// completes whatever the residency; the flags are cleared on exit so a graph
+// replay (same tag) starts from clear flags.
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV>
+__global__ void __launch_bounds__(NW * 64) chunk_kernel_seg(ChunkArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW>::BYTES];
+  __shared__ unsigned long long s_todo;
+  constexpr int NBLK = DV / BN;
+  const int xb = blockIdx.x;
+  const int nseg = a.nseg;
+  const int seg = (xb >> 3) % nseg;
+  const int slot2 = (xb >> 3) / nseg;
+  const int64_t bh = (int64_t)(slot2 / NBLK) * 8 + (xb & 7);
+  if (bh >= a.B * a.H) return;
+  unsigned long long* const flag = a.seg_flag + (bh * NBLK + slot2 % NBLK) * nseg;
+  const int wi = REV ? nseg - 1 - seg : seg;  // position in walk order
+  const unsigned long long tag = a.seg_tag | xcc_id();
+  unsigned long long todo = 0;  // earlier segments still to form here (bit = walk position)
+  int job = wi;                 // walk position of the state pass to run next
+  for (bool own = true;; own = false) {
+    if (job < nseg - 1) {  // the last segment in walk order has no state pass
+      __syncthreads();     // LDS free for the next pass
+      const int sj = REV ? nseg - 1 - job : job;
+      chunk_body<DK, DV, BN, NW, C, NT, REV, true>(a, xb + 8 * (sj - seg), smem);
+    }
+    if (own) {
+      if (wi < nseg - 1) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's state stores are in L2
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(flag + seg, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (threadIdx.x < 64) {  // wave 0, lane p polls the flag of walk position p
+        const int p = threadIdx.x;
+        const int sp = REV ? nseg - 1 - p : p;
+        bool done = p >= wi, miss = false;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (int it = 0;; ++it) {
+          if (!done) {
+            const unsigned long long f = __hip_atomic_load(flag + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (f == tag) {
+              done = true;
+            } else if ((f & ~0xffull) == a.seg_tag) {  // published from another XCD: not in this L2
+              done = true;
+              miss = true;
+            }
+          }
+          if (__all(done)) break;
+          if (it >= (1 << 20) || __builtin_amdgcn_s_memrealtime() - t0 > a.seg_wait) {
+            miss = miss || !done;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        const unsigned long long m = __ballot(miss);
+        if (p == 0) s_todo = m;
+      }
+      __syncthreads();
+      todo = s_todo;
+    }
+    if (todo == 0) break;
+    job = __builtin_ctzll(todo);
+    todo &= todo - 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // states formed here are in L2 too
+  __syncthreads();
+  chunk_body<DK, DV, BN, NW, C, NT, REV, false, false, false, true>(a, xb, smem);
+  if (wi < nseg - 1 && threadIdx.x == 0)
+    __hip_atomic_store(flag + seg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Two independent passes of one shape in one launch, the first in forward
@@ -1178,6 +1308,10 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const int64_t nblocks = groups * 8 * NBLK * a.nseg;
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)nblocks), block(NW * 64);
+  if (a.nseg > 1 && a.seg_flag != nullptr && !a.reverse && a.cu == nullptr && a.pool == nullptr) {
+    hipLaunchKernelGGL((chunk_kernel_seg<DK, DV, BN, NW, C, NT, false>), grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   if (a.nseg > 1) {
     if (a.reverse) hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, true, true>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((chunk_kernel<DK, DV, BN, NW, C, NT, false, true>), grid, block, 0, st, a);

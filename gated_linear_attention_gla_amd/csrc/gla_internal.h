@@ -37,6 +37,15 @@ struct ChunkArgs {
   int nseg;
   int64_t seg_len;
   float* seg_state;
+  // One-launch split (seg_flag set): every workgroup runs its own segment's
+  // state pass, publishes it with its flag (index (bh NBLK + column block)
+  // nseg + segment) set to seg_tag | the XCD it ran on, and folds an earlier
+  // segment's state once that flag reads the same tag and XCD (same L2);
+  // after seg_wait ticks of the 100 MHz clock it forms the state itself.
+  // Each workgroup clears its flag on exit.
+  unsigned long long* seg_flag;
+  unsigned long long seg_tag;  // per-call nonzero epoch << 8
+  uint32_t seg_wait;
   // Packed variable-length mode (prefill into the decode state pool).  With
   // cu set, unit b covers tokens [cu[b], cu[b+1]) of the packed inputs
   // (clamped to [0, T]; stride_b is then 0).  With pool set, unit (b, h)

@@ -106,12 +106,24 @@ const char* gla_status_string(gla_status s);
  * When B * H is too small to occupy the GPU, a pass splits every sequence
  * into nseg segments of whole chunks (2 <= nseg <= 64, at least two chunks
  * each; page section "Challenge 1": the chunks are independent apart from the
- * state they hand on).  A first launch writes each segment's end state from a
- * zero start; the second starts segment j from the decayed sum of the end
- * states before it.  The workspace holds those states: B*H*nseg*dk*dv fp32
- * values; ws must be 16-byte aligned (GLA_ERR_WORKSPACE otherwise).  Its
- * contents are scratch and are not needed after the call completes. */
+ * state they hand on).  Each segment's end state from a zero start is written
+ * to the workspace, and segment j starts from the decayed sum of the end
+ * states before it.  gla_chunk_fwd does both in one launch: a workgroup
+ * publishes its segment's end state with an 8-byte flag and reads the earlier
+ * ones once their flags are set.  The workspace holds B*H*nseg*dk*dv fp32
+ * states followed by B*H*nseg*ceil(dv/16) flags; ws must be 16-byte aligned
+ * (GLA_ERR_WORKSPACE otherwise).  Nothing in it needs to start at zero (a
+ * flag counts only if it carries the call's own tag) and its contents are
+ * not needed after the call completes. */
 size_t gla_chunk_fwd_workspace(const gla_dims* dims);
+
+/* Tuning of the one-launch segment split in gla_chunk_fwd: how long, in
+ * microseconds, a workgroup waits for an earlier segment's end state before
+ * forming that state itself (by the same arithmetic, so results never
+ * depend on it).  Negative restores the default, about four times a
+ * segment's state pass; 0 forms at once every state not yet published.
+ * Process-wide; takes effect for calls made after it. */
+void gla_set_segment_wait(int32_t microseconds);
 
 /* Chunked forward (page sections "GLA mixer" and "Challenge 1").
  *   q [B,H,T,dk], k [B,H,T,dk], v [B,H,T,dv]   inputs (gla_tensor views)
@@ -141,7 +153,8 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const gla_tensor* q, const gla_te
  *   Limit   dims whose gla_chunk_fwd_workspace() exceeds the scratch return
  *           GLA_ERR_WORKSPACE before anything is enqueued; at dk=96, dv=192
  *           that is B*H in 114..127 with T of at least 4 chunks (254 segment
- *           states of 73,728 bytes at most, against 227 that fit).
+ *           states of 73,728 bytes, with 96 bytes of flags each, at most,
+ *           against 227 that fit).
  *   Sharing Every call on one GPU uses the same scratch: calls that overlap
  *           on that GPU (different streams or host threads without ordering)
  *           race and must be serialised by the caller.  Calls ordered on one

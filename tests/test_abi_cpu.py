@@ -133,11 +133,12 @@ def test_workspace_queries(lib):
 
 
 def test_workspace_segment_rule(lib):
-    """The workspace holds one fp32 dk x dv end state per (b, h, segment).  No
-    split when the (b, h, column block) units already fill the GPU or the
-    sequence has fewer than 4 chunks; otherwise 2 to 64 segments of at least
-    2 whole chunks, and the segment length never leaves an empty segment."""
-    per = lambda B, H: B * H * 96 * 192 * 4
+    """The workspace holds one fp32 dk x dv end state and dv / 16 8-byte flags
+    per (b, h, segment).  No split when the (b, h, column block) units
+    already fill the GPU or the sequence has fewer than 4 chunks; otherwise
+    2 to 64 segments of at least 2 whole chunks, and the segment length never
+    leaves an empty segment."""
+    per = lambda B, H: B * H * (96 * 192 * 4 + 192 // 16 * 8)
     q = lambda **kw: lib.gla_chunk_fwd_workspace(ctypes.byref(dims(dk=96, dv=192, **kw)))
     assert q(B=8, H=16, Tn=2048, chunk=128) == 0           # 256 units: no split
     assert q(B=1, H=16, Tn=3 * 128, chunk=128) == 0        # 3 chunks: no split
@@ -177,17 +178,18 @@ def fwd_noalloc(lib, d, q, k, v, o, lam=0x9000, S0=None, ST=None):
 def test_fwd_noalloc_validation(lib):
     """The allocation-free forward validates like gla_chunk_fwd, and rejects
     dims whose segment states exceed its 16 MiB static scratch before any HIP
-    call: B*H = 120 at (96, 192) over 4 chunks needs 240 states of 73,728 B."""
+    call: B*H = 120 at (96, 192) over 4 chunks needs 240 states of 73,728 B
+    (and 96 B of flags each)."""
     assert lib.gla_chunk_fwd_noalloc.restype is ctypes.c_int
     q, k, v, o = views(H=120, Tn=256)
     d = dims(H=120, Tn=256, chunk=64)
     need = lib.gla_chunk_fwd_workspace(ctypes.byref(d))
-    assert need == 120 * 2 * 96 * 192 * 4 > 16 << 20
+    assert need == 120 * 2 * (96 * 192 * 4 + 96) > 16 << 20
     assert fwd_noalloc(lib, d, q, k, v, o) == WS
     # the largest B*H that still fits: 113 heads, 226 states
     q2, k2, v2, o2 = views(H=113, Tn=256)
     d2 = dims(H=113, Tn=256, chunk=64)
-    assert lib.gla_chunk_fwd_workspace(ctypes.byref(d2)) == 226 * 96 * 192 * 4 <= 16 << 20
+    assert lib.gla_chunk_fwd_workspace(ctypes.byref(d2)) == 226 * (96 * 192 * 4 + 96) <= 16 << 20
     # ordinary validation comes first and is the same as gla_chunk_fwd's
     assert fwd_noalloc(lib, None, q, k, v, o) == NULL
     assert fwd_noalloc(lib, d, q, k, v, o, lam=None) == NULL

@@ -309,10 +309,13 @@ def test_fwd_bwd_half_decay_fp32(gla, chunk):
 # is ragged, segments are dropped by the rounding of the segment length, and
 # the reverse-time passes of the backward carry dS0 across segments.
 def segments_of(gla, B, H, T, dk, dv, chunk, bwd=False):
-    """Segments per (b, h) implied by the workspace query (end states, fp32)."""
+    """Segments per (b, h) implied by the workspace query (fp32 end states;
+    the forward adds dv / 16 8-byte flags per state)."""
     lib, d = gla.load_library(), ctypes.byref(gla.GlaDims(B, H, T, dk, dv, chunk))
     nws = lib.gla_chunk_bwd_workspace(d) if bwd else lib.gla_chunk_fwd_workspace(d)
-    return nws // (B * H * dk * dv * 4)
+    per = dk * dv * 4 + (0 if bwd else -(-dv // 16) * 8)
+    assert nws % (B * H * per) == 0
+    return nws // (B * H * per)
 
 
 @pytest.mark.parametrize("T,chunk", [(1000, 32), (1000, 128), (9 * 64 - 5, 64), (4 * 16, 16)])
@@ -342,6 +345,68 @@ def test_fwd_segments_long_decay(gla):
     x["S0"] = inputs.normal(411, inputs.TID["S"], (1, 2, 96, 192), 0.01, "f32")
     assert segments_of(gla, 1, 2, 16384, 96, 192, 128) == 64
     check_fwd(gla, x, "bf16", 128)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 96, 192, "bf16", 64), (1, 1, 1500, 16, 32, "f32", 16)])
+def test_fwd_segments_without_waiting(gla, shape):
+    """The forward publishes each segment's end state within its one launch;
+    with no wait at all, a workgroup forms every earlier state it finds
+    unpublished itself.  The arithmetic is the same either way, so the
+    outputs equal those of the default wait bit for bit (and pass the gate)."""
+    B, H, T, dk, dv, dtype, chunk = shape
+    flush(f"test_fwd_segments_without_waiting {shape}")
+    x = inputs.random_chunk_inputs(450 + T, B, H, T, dk, dv, dtype=dtype, scale=0.3)
+    assert segments_of(gla, B, H, T, dk, dv, chunk) >= 2
+    base = run_fwd(gla, x, dtype, chunk)
+    try:
+        gla.set_segment_wait(0)
+        forced = run_fwd(gla, x, dtype, chunk)
+        forced2 = run_fwd(gla, x, dtype, chunk)
+    finally:
+        gla.set_segment_wait(-1)
+    for got in (forced, forced2):
+        assert np.array_equal(got[0], base[0]) and np.array_equal(got[1], base[1])
+    ro, rS = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], x["S0"])
+    assert oracle.rel_err(base[0], ro) <= TOL[dtype] and oracle.rel_err(base[1], rS) <= TOL[dtype]
+
+
+def test_fwd_segments_graph_replays(gla):
+    """A captured segmented forward replays with the tag of its capture: each
+    replay, with new inputs copied in and eager calls in between, must equal
+    the eager result bit for bit (no replay may take a flag left by the one
+    before it)."""
+    flush("test_fwd_segments_graph_replays")
+    B, H, T, chunk = 1, 2, 777, 64
+    assert segments_of(gla, B, H, T, 96, 192, chunk) >= 2
+    sets = [inputs.random_chunk_inputs(460 + i, B, H, T, 96, 192, dtype="bf16", scale=0.3) for i in range(3)]
+    q, k, v = (dev(sets[0][n], "bf16") for n in ("q", "k", "v"))
+    lam, S0 = dev_f32(sets[0]["lam"]), dev_f32(sets[0]["S0"])
+    o = torch.empty((B, H, T, 192), dtype=torch.float32, device="cuda")
+    S = torch.empty((B, H, 96, 192), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, o=o, S_T=S)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, o=o, S_T=S)
+    torch.cuda.synchronize()
+    for i in range(6):
+        x = sets[i % 3]
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            t.copy_(dev(x[name], "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_S = host(o), host(S)
+        eo, eS = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert np.array_equal(got_o, host(eo)) and np.array_equal(got_S, host(eS)), f"replay {i}"
+    # the decay and entry state stay those of the first set
+    ro, rS = oracle.fwd(x["q"], x["k"], x["v"], sets[0]["lam"], sets[0]["S0"])
+    assert oracle.rel_err(got_o, ro) <= TOL["bf16"] and oracle.rel_err(got_S, rS) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("T,chunk", [(777, 64), (1000, 128), (300, 32)])
