@@ -90,9 +90,18 @@ int64_t seg_len_for(int64_t T, int64_t chunk, int nseg) {
   return ((nchunks + nseg - 1) / nseg) * chunk;
 }
 
+// Segments of a pass of this shape; the workspace queries take no dtype, so
+// they size for the larger count of the two input dtypes (the tiling, and
+// with it the count, can differ between them).
+int max_segments(const gla_dims* d, int dk, int dv) {
+  const int a = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk, 0);
+  const int b = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk, 1);
+  return a > b ? a : b;
+}
+
 // Workspace of one segment-split pass: the end state of every (b, h, segment).
 size_t pass_workspace(const gla_dims* d, int dk, int dv) {
-  const int nseg = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk);
+  const int nseg = max_segments(d, dk, dv);
   if (nseg <= 1) return 0;
   return (size_t)d->B * d->H * nseg * d->dk * d->dv * sizeof(float);
 }
@@ -100,7 +109,7 @@ size_t pass_workspace(const gla_dims* d, int dk, int dv) {
 // Flags of a one-launch segment split: one 8-byte word per (b, h, column
 // block, segment), with at most dv / 16 column blocks.
 size_t seg_flag_bytes(const gla_dims* d, int dv) {
-  const int nseg = gla::chunk_segments(d->B, d->H, d->T, (int)d->dk, dv, (int)d->chunk);
+  const int nseg = max_segments(d, (int)d->dk, dv);
   if (nseg <= 1) return 0;
   return (size_t)d->B * d->H * nseg * ((dv + 15) / 16) * sizeof(unsigned long long);
 }
@@ -132,7 +141,7 @@ uint32_t seg_wait_ticks(int64_t seg_chunks) {
 }
 
 void set_segments(ChunkArgs& a, const gla_dims* d, int dk, int dv, void* ws) {
-  a.nseg = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk);
+  a.nseg = gla::chunk_segments(d->B, d->H, d->T, dk, dv, (int)d->chunk, a.in_f32);
   a.seg_len = a.nseg > 1 ? seg_len_for(d->T, d->chunk, a.nseg) : (d->T > 0 ? d->T : 1);
   a.seg_state = a.nseg > 1 ? static_cast<float*>(ws) : nullptr;
 }

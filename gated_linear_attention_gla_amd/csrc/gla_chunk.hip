@@ -1397,13 +1397,6 @@ hipError_t launch_chunk_fused(int dk, int dv, int chunk, const ChunkArgs& a, hip
   }
 }
 
-// column-block width per shape and chunk (must match launch_shape)
-static int block_cols(int dk, int dv, int chunk) {
-  if (dk == 96 && dv == 192) return 96;
-  if (dk == 192 && dv == 96) return chunk <= 64 ? 96 : 48;
-  return dv;  // the small shapes run all columns in one workgroup
-}
-
 int segments_for_units(int64_t units, int64_t T, int chunk) {
   constexpr int64_t kTargetUnits = 256;  // one workgroup per compute unit of an MI355X
   const int64_t nchunks = (T + chunk - 1) / chunk;
@@ -1417,8 +1410,30 @@ int segments_for_units(int64_t units, int64_t T, int chunk) {
   return (int)((nchunks + seg_chunks - 1) / seg_chunks);
 }
 
-int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk) {
-  const int nblk = dv / block_cols(dk, dv, chunk);
+// (96, 192) with fewer than 128 (b, h) units and long segments: all 192
+// columns in one 12-wave workgroup.  It runs a chunk of the whole head in
+// about 1.6 times what the 6-wave tiling takes for half of it and reads k
+// once, but leaves half as many workgroups per segment, so it is used where
+// the split still leaves at least 8 chunks per segment (the state pass and
+// fold grow with the segment count).  fp32 inputs fit its LDS up to
+// 32-token chunks.
+static bool wide_tiles(int dk, int dv, int chunk, int in_f32, int64_t BH, int64_t T) {
+  if (!(dk == 96 && dv == 192) || BH >= 128 || chunk > (in_f32 ? 32 : 64)) return false;
+  const int64_t nchunks = (T + chunk - 1) / chunk;
+  return nchunks >= 8 * (int64_t)segments_for_units(BH, T, chunk);
+}
+
+// column-block width per shape and chunk (must match launch_shape)
+static int block_cols(int dk, int dv, int chunk, int in_f32, int64_t BH, int64_t T) {
+  if (wide_tiles(dk, dv, chunk, in_f32, BH, T)) return 192;
+  if (dk == 96 && dv == 192) return 96;
+  if (dk == 192 && dv == 96) return chunk <= 64 ? 96 : 48;
+  return dv;  // the small shapes run all columns in one workgroup
+}
+
+
+int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk, int in_f32) {
+  const int nblk = dv / block_cols(dk, dv, chunk, in_f32, B * H, T);
   // the backward's two transposed passes share one launch when each has a
   // single column block (launch_tiles)
   return segments_for_units(B * H * nblk * ((dk > dv && nblk == 1) ? 2 : 1), T, chunk);
@@ -1445,7 +1460,13 @@ static hipError_t launch_tiles(const ChunkArgs& a, const ChunkArgs* a1, hipStrea
 // Tile shapes per (DK, DV): BN columns per workgroup, NW waves.
 template <int DK, int DV, int C, int NT>
 static hipError_t launch_shape(const ChunkArgs& a, const ChunkArgs* a1, hipStream_t st) {
-  if constexpr (DK == 96 && DV == 192) return launch_tiles<96, 192, 96, 6, C, NT>(a, a1, st);
+  if constexpr (DK == 96 && DV == 192) {
+    if constexpr (C <= (NT == 1 ? 64 : 32)) {
+      if (a.cu == nullptr && a.pool == nullptr && wide_tiles(DK, DV, C, a.in_f32, a.B * a.H, a.T))
+        return launch_tiles<96, 192, 192, 12, C, NT>(a, a1, st);
+    }
+    return launch_tiles<96, 192, 96, 6, C, NT>(a, a1, st);
+  }
   else if constexpr (DK == 192 && DV == 96) {
     // bf16 inputs up to 64-token chunks: all 96 columns on 12 waves, each
     // 16-column strip shared by two waves that own 96 state rows each (three

@@ -117,7 +117,8 @@ def test_fwd_laplace_full(gla, chunk):
 def test_fwd_long_context_full(gla):
     """Long-context prefill at its full size (B=1, H=16, T=65,536, bf16,
     lambda in [0.95, 0.9999]) in the launch configurations the benchmark times
-    (64- and 128-token chunks, 8 segments per head): the whole fp32-stored
+    (64-token chunks: all 192 columns per workgroup, 16 segments per head;
+    128-token chunks: two column blocks, 8 segments): the whole fp32-stored
     output and the final state against the oracle, and the bf16-stored output
     equal to the fp32-stored one rounded to nearest, within one bf16 ulp."""
     flush("test_fwd_long_context_full T=65536")
@@ -126,7 +127,7 @@ def test_fwd_long_context_full(gla):
     q, k, v = dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16")
     lam, S0 = dev_f32(x["lam"]), dev_f32(x["S0"])
     for chunk in (64, 128):
-        assert segments_of(gla, 1, 16, 65536, 96, 192, chunk) >= 2
+        assert segments_of(gla, 1, 16, 65536, 96, 192, chunk) == (16 if chunk == 64 else 8)
         o32, S32 = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.float32)
         o16, _ = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
@@ -407,6 +408,20 @@ def test_fwd_segments_graph_replays(gla):
     # the decay and entry state stay those of the first set
     ro, rS = oracle.fwd(x["q"], x["k"], x["v"], sets[0]["lam"], sets[0]["S0"])
     assert oracle.rel_err(got_o, ro) <= TOL["bf16"] and oracle.rel_err(got_S, rS) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,chunk,T", [("bf16", 16, 8192 + 37), ("f32", 32, 16384 + 5), ("bf16", 64, 32768 - 11)])
+def test_wide_tiles_fwd_bwd(gla, dtype, chunk, T):
+    """Few (b, h) units with at least 8 chunks per segment: the (96, 192)
+    passes run all 192 columns of a head in one 12-wave workgroup (the
+    forward, and the backward's dv pass).  Ragged T, up to 64 segments,
+    fp32 up to its 32-token limit for that tiling."""
+    flush(f"test_wide_tiles_fwd_bwd {dtype} chunk={chunk} T={T}")
+    x = inputs.random_chunk_inputs(470 + chunk, 1, 2, T, 96, 192, dtype=dtype, dS_T=True, scale=0.3)
+    n, nchunks = segments_of(gla, 1, 2, T, 96, 192, chunk), -(-T // chunk)
+    assert 2 <= n <= 64 and nchunks >= 8 * n
+    check_fwd(gla, x, dtype, chunk)
+    check_bwd(gla, x, dtype, chunk)
 
 
 @pytest.mark.parametrize("T,chunk", [(777, 64), (1000, 128), (300, 32)])
