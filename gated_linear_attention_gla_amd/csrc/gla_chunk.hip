@@ -265,11 +265,19 @@ struct ChunkLds {
 // One chunk pass for workgroup slot xb of a launch (the whole body of the
 // kernels below).  SO (state only): the segment state pass -- only the state
 // update runs, from a zero state, and the segment's end state goes to
-// a.seg_state.  MRG: the earlier segments' states were written in this same
-// launch, by other workgroups on this XCD, and are read from L2.
+// a.seg_state.  MRG: the earlier segments' states are written in this same
+// launch, by other workgroups on this XCD, and read from L2; wait_entry()
+// returns once they are all available, and is called after this pass's
+// first tiles and entry state have been requested, so those loads and the
+// tables overlap the wait.
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
 template <int DK, int DV, int BN, int NW, int C, int NT, bool REV, bool SO, bool EPI = false, bool PACKED = false,
-          bool MRG = false>
-__device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, char* const smem) {
+          bool MRG = false, typename Wait = NoWait>
+__device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, char* const smem,
+                                           const Wait& wait_entry = Wait{}) {
   using Lds = ChunkLds<DK, BN, C, NT, NW, EPI>;
   constexpr int NTHR = NW * 64;
   // Row split (RS > 1): RS waves share each 16-column strip, wave half rh
@@ -494,7 +502,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // states: S <- lam^len S + E, oldest first.  Every such segment is whole
   // except, in reverse time, the last one (walked first), so two powers
   // serve them all.
-  if constexpr (!SO) {
+  auto fold_entry = [&]() {
     const int first = REV ? nseg - 1 : 0;
     const int step = REV ? -1 : 1;
     const int64_t tail = T - (int64_t)(nseg - 1) * a.seg_len;  // the last segment's length
@@ -544,13 +552,22 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           }
       }
     }
+  };
+  // Workgroups of up to two waves per SIMD wait once the first tiles are
+  // requested too (below); with three, the tiles' registers held through the
+  // wait would spill.
+  constexpr bool EARLY = MRG && NW <= 8;
+  if constexpr (!SO && !MRG) fold_entry();
+  if constexpr (MRG && !EARLY) {
+    wait_entry();
+    fold_entry();
   }
 
   // The entry state has landed before the chunk loop starts.  (Without this
   // explicit wait the compiler cannot prove it on every path into the loop
   // and waits for all outstanding global loads -- including the next chunk's
   // prefetch -- at the first use of the state in every iteration.)
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unchanged
+  if constexpr (!EARLY) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unchanged
 
   // writes 4 consecutive masked-P values of row i (cols 16 J + 4 g ..) as NTP planes
   auto put_p = [&](int i, int J, const f32x4& val) {
@@ -638,9 +655,21 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // chunk ci is computed and written to LDS as soon as its last reader is
   // done; the output of chunk ci is stored last, so its write latency
   // overlaps the compute of chunk ci+1.
+  if constexpr (EARLY) {
+    if (nchunks == 0) {
+      wait_entry();
+      fold_entry();
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+  }
   if (nchunks > 0) {
     if constexpr (!SO) prefetch_q(0);
     prefetch_kv(0);
+    if constexpr (EARLY) {
+      wait_entry();
+      fold_entry();
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): entry state and first tiles
+    }
     if constexpr (!SO) pfq.store(sQ, tid);
     pfk.store(sK, tid);
     pfv.store(sV, tid);
@@ -1212,16 +1241,17 @@ __device__ __forceinline__ unsigned xcc_id() {
 
 // A segment split in one launch.  Workgroup (unit, segment) first runs its
 // segment's state pass and publishes the end state (stores drained to L2,
-// then the flag); then one lane polls the flags of the segments before it in
-// walk order, which sit 8 (segment distance) workgroups earlier in dispatch
-// order and so -- workgroups being dealt to the XCDs in turn -- on the same
-// XCD, sharing its L2.  A flag counts only if it carries this call's tag and
-// this XCD's id.  Any earlier state not published within a.seg_wait ticks
-// (the producer not resident, or on another XCD) is formed here by the same
-// state pass, bit for bit what its producer writes.  Then the full pass folds
-// them in as in the two-launch form.  Every wait is bounded, so the launch
-// completes whatever the residency; the flags are cleared on exit so a graph
-// replay (same tag) starts from clear flags.
+// then the flag).  Its full pass then fills its tables and requests its
+// entry state and first tiles before it waits: lane p of wave 0 polls the
+// flag of walk position p, whose workgroup sits 8 (segment distance) block
+// ids earlier and so -- workgroups being dealt to the XCDs in turn -- on the
+// same XCD, sharing its L2.  A flag counts only if it carries this call's
+// tag and this XCD's id.  Any earlier state not published within a.seg_wait
+// ticks (the producer not resident, or on another XCD) is formed here by the
+// same state pass, bit for bit what its producer writes.  Then the full pass
+// folds them in as in the two-launch form.  Every wait is bounded, so the
+// launch completes whatever the residency; the flags are cleared on exit so a
+// graph replay (same tag) starts from clear flags.
 template <int DK, int DV, int BN, int NW, int C, int NT, bool REV>
 __global__ void __launch_bounds__(NW * 64) chunk_kernel_seg(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW>::BYTES];
@@ -1236,55 +1266,66 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel_seg(ChunkArgs a) {
   unsigned long long* const flag = a.seg_flag + (bh * NBLK + slot2 % NBLK) * nseg;
   const int wi = REV ? nseg - 1 - seg : seg;  // position in walk order
   const unsigned long long tag = a.seg_tag | xcc_id();
-  unsigned long long todo = 0;  // earlier segments still to form here (bit = walk position)
-  int job = wi;                 // walk position of the state pass to run next
-  for (bool own = true;; own = false) {
-    if (job < nseg - 1) {  // the last segment in walk order has no state pass
-      __syncthreads();     // LDS free for the next pass
-      const int sj = REV ? nseg - 1 - job : job;
-      chunk_body<DK, DV, BN, NW, C, NT, REV, true>(a, xb + 8 * (sj - seg), smem);
-    }
-    if (own) {
-      if (wi < nseg - 1) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's state stores are in L2
-        __syncthreads();
-        if (threadIdx.x == 0) __hip_atomic_store(flag + seg, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (threadIdx.x < 64) {  // wave 0, lane p polls the flag of walk position p
-        const int p = threadIdx.x;
-        const int sp = REV ? nseg - 1 - p : p;
-        bool done = p >= wi, miss = false;
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        for (int it = 0;; ++it) {
-          if (!done) {
-            const unsigned long long f = __hip_atomic_load(flag + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (f == tag) {
-              done = true;
-            } else if ((f & ~0xffull) == a.seg_tag) {  // published from another XCD: not in this L2
-              done = true;
-              miss = true;
-            }
-          }
-          if (__all(done)) break;
-          if (it >= (1 << 20) || __builtin_amdgcn_s_memrealtime() - t0 > a.seg_wait) {
-            miss = miss || !done;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        const unsigned long long m = __ballot(miss);
-        if (p == 0) s_todo = m;
-      }
-      __syncthreads();
-      todo = s_todo;
-    }
-    if (todo == 0) break;
-    job = __builtin_ctzll(todo);
-    todo &= todo - 1;
+  // this segment's end state from a zero start (the last segment in walk
+  // order has none), published once its stores are in L2
+  if (wi < nseg - 1) {
+    chunk_body<DK, DV, BN, NW, C, NT, REV, true>(a, xb, smem);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's state stores are in L2
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag + seg, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // LDS free for the full pass
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // states formed here are in L2 too
-  __syncthreads();
-  chunk_body<DK, DV, BN, NW, C, NT, REV, false, false, false, true>(a, xb, smem);
+  // Called by the full pass once its own loads are in flight: every earlier
+  // state published here, or formed by this workgroup.
+  auto wait_entry = [&]() {
+    if (threadIdx.x < 64) {  // wave 0, lane p polls the flag of walk position p
+      const int p = threadIdx.x;
+      const int sp = REV ? nseg - 1 - p : p;
+      bool done = p >= wi, miss = false;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (int it = 0;; ++it) {
+        if (!done) {
+          const unsigned long long f = __hip_atomic_load(flag + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (f == tag) {
+            done = true;
+          } else if ((f & ~0xffull) == a.seg_tag) {  // published from another XCD: not in this L2
+            done = true;
+            miss = true;
+          }
+        }
+        if (__all(done)) break;
+        if (it >= (1 << 20) || __builtin_amdgcn_s_memrealtime() - t0 > a.seg_wait) {
+          miss = miss || !done;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      const unsigned long long m = __ballot(miss);
+      if (p == 0) s_todo = m;
+    }
+    __syncthreads();
+    unsigned long long todo = s_todo;
+    if (todo != 0) {
+      // the full pass has put only its power table (the same values) in LDS
+      do {
+        const int job = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int sj = REV ? nseg - 1 - job : job;
+        __syncthreads();
+        chunk_body<DK, DV, BN, NW, C, NT, REV, true>(a, xb + 8 * (sj - seg), smem);
+      } while (todo != 0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // states formed here are in L2 too
+      __syncthreads();
+    }
+  };
+  if constexpr (NW <= 8) {
+    chunk_body<DK, DV, BN, NW, C, NT, REV, false, false, false, true>(a, xb, smem, wait_entry);
+  } else {
+    // (the full pass of three waves per SIMD has no registers to spare for
+    // its own loads across the wait: it starts after it)
+    wait_entry();
+    chunk_body<DK, DV, BN, NW, C, NT, REV, false, false, false, true>(a, xb, smem);
+  }
   if (wi < nseg - 1 && threadIdx.x == 0)
     __hip_atomic_store(flag + seg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
