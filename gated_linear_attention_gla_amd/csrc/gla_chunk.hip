@@ -428,7 +428,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   constexpr bool rev = REV;  // time direction (a.reverse selected this instantiation)
 
   const float lam = a.lam[h];
-  for (int n = tid; n <= CP + 1; n += NTHR) sPow[n] = lam_pow_f32(lam, n);
+  // (a one-launch full pass after its own state pass finds the table in LDS;
+  // state passes formed during its wait write the same values)
+  if (!(MRG && seg != (REV ? 0 : nseg - 1)))
+    for (int n = tid; n <= CP + 1; n += NTHR) sPow[n] = lam_pow_f32(lam, n);
   // epilogue: the head's channel scales, zeroed row-sum padding, and this
   // lane's RMSNorm weights (output columns (w NS + s) 16 + 4 g + r)
   float gam[NS][4];
@@ -482,7 +485,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // ---- state slice in accumulators: accS[Do][s][r] = S[state_row(D)][col0 + 16 s]
   // for this wave's row tiles D = rh DKTO + Do
   f32x4 accS[DKTO][NS];
-  {
+  auto load_entry = [&]() {
     const float* si = SO ? nullptr : s_init;
 #pragma unroll
     for (int Do = 0; Do < DKTO; ++Do)
@@ -497,7 +500,17 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           if (si) x = a.s_init_trans ? si[(int64_t)n * DK + d] : si[(int64_t)d * DV + n];
           accS[Do][s][r] = x;
         }
-  }
+  };
+  // Workgroups of up to two waves per SIMD wait inside the chunk-loop
+  // prologue (below); with three, the tiles' registers held through the wait
+  // would spill.  The last segment in walk order has no state pass of its
+  // own: it requests its entry state and first tiles before it waits, while
+  // the others run their state passes.  The others reach the wait just as
+  // the flags are due and poll with no loads of their own in flight (a wait
+  // for a load is a wait for every load issued before it).
+  constexpr bool EARLY = MRG && NW <= 8;
+  const bool idle_wait = seg == (REV ? 0 : nseg - 1);
+  if (!EARLY || idle_wait) load_entry();
   // The segments before this one (in walk order) enter through their end
   // states: S <- lam^len S + E, oldest first.  Every such segment is whole
   // except, in reverse time, the last one (walked first), so two powers
@@ -553,10 +566,6 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       }
     }
   };
-  // Workgroups of up to two waves per SIMD wait once the first tiles are
-  // requested too (below); with three, the tiles' registers held through the
-  // wait would spill.
-  constexpr bool EARLY = MRG && NW <= 8;
   if constexpr (!SO && !MRG) fold_entry();
   if constexpr (MRG && !EARLY) {
     wait_entry();
@@ -656,19 +665,25 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   // done; the output of chunk ci is stored last, so its write latency
   // overlaps the compute of chunk ci+1.
   if constexpr (EARLY) {
-    if (nchunks == 0) {
-      wait_entry();
-      fold_entry();
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (nchunks > 0 && idle_wait) {
+      prefetch_q(0);
+      prefetch_kv(0);
     }
+    wait_entry();
+    if (!idle_wait) {
+      load_entry();
+      if (nchunks > 0) {
+        prefetch_q(0);
+        prefetch_kv(0);
+      }
+    }
+    fold_entry();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): entry state and first tiles
   }
   if (nchunks > 0) {
-    if constexpr (!SO) prefetch_q(0);
-    prefetch_kv(0);
-    if constexpr (EARLY) {
-      wait_entry();
-      fold_entry();
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): entry state and first tiles
+    if constexpr (!EARLY) {
+      if constexpr (!SO) prefetch_q(0);
+      prefetch_kv(0);
     }
     if constexpr (!SO) pfq.store(sQ, tid);
     pfk.store(sK, tid);
