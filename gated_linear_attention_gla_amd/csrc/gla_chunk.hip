@@ -26,6 +26,7 @@
 // Operands that are not exact bf16 values (the masked P tile, the state, the
 // decay-scaled values) enter the MFMA as hi+lo bf16 pairs (three terms for fp32
 // inputs), which keeps every product at fp32-level accuracy.
+#include <atomic>
 #include <type_traits>
 
 #include "gla_common.hpp"
@@ -1356,6 +1357,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel_pair(ChunkArgs a0, Chunk
   else chunk_body<DK, DV, BN, NW, C, NT, true, SO>(a1, xb - nb0, smem);
 }
 
+// Compute units of the device that runs stream st, looked up once per
+// device (0 if that fails).
+static int device_cus(hipStream_t st) {
+  static std::atomic<int> cache[64];
+  int dev = -1;
+  const hipError_t e = st == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int DK, int DV, int BN, int NW, int C, int NT>
 static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   constexpr int NBLK = DV / BN;
@@ -1364,7 +1380,11 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const int64_t nblocks = groups * 8 * NBLK * a.nseg;
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)nblocks), block(NW * 64);
-  if (a.nseg > 1 && a.seg_flag != nullptr && !a.reverse && a.cu == nullptr && a.pool == nullptr) {
+  // One launch only while every workgroup can hold a compute unit of its
+  // own: a workgroup that waits on a segment whose workgroup is still queued
+  // behind it would hold its unit idle (two launches are faster then).
+  if (a.nseg > 1 && a.seg_flag != nullptr && !a.reverse && a.cu == nullptr && a.pool == nullptr &&
+      BH * NBLK * a.nseg <= device_cus(st)) {
     hipLaunchKernelGGL((chunk_kernel_seg<DK, DV, BN, NW, C, NT, false>), grid, block, 0, st, a);
     return hipGetLastError();
   }

@@ -371,6 +371,17 @@ def test_fwd_segments_without_waiting(gla, shape):
     assert oracle.rel_err(base[0], ro) <= TOL[dtype] and oracle.rel_err(base[1], rS) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("B,H,T", [(4, 25, 640 - 3), (1, 127, 300)])
+def test_fwd_segments_more_workgroups_than_cus(gla, B, H, T):
+    """Two segments per (b, h) with 100 and 127 heads: 400 and 508 workgroups
+    of the one-launch forward, more than one per compute unit, so some wait
+    on earlier segments that are resident while others are still queued."""
+    flush(f"test_fwd_segments_more_workgroups_than_cus B={B} H={H} T={T}")
+    x = inputs.random_chunk_inputs(480 + H, B, H, T, 96, 192, dtype="bf16", scale=0.3)
+    assert segments_of(gla, B, H, T, 96, 192, 64) == 2
+    check_fwd(gla, x, "bf16", 64)
+
+
 def test_fwd_segments_graph_replays(gla):
     """A captured segmented forward replays with the tag of its capture: each
     replay, with new inputs copied in and eager calls in between, must equal
