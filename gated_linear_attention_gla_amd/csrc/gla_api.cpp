@@ -108,10 +108,16 @@ size_t pass_workspace(const gla_dims* d, int dk, int dv) {
 
 // Flags of a one-launch segment split: one 8-byte word per (b, h, column
 // block, segment), with at most dv / 16 column blocks.
-size_t seg_flag_bytes(const gla_dims* d, int dv) {
-  const int nseg = max_segments(d, (int)d->dk, dv);
+size_t seg_flag_bytes(const gla_dims* d, int dk, int dv) {
+  const int nseg = max_segments(d, dk, dv);
   if (nseg <= 1) return 0;
   return (size_t)d->B * d->H * nseg * ((dv + 15) / 16) * sizeof(unsigned long long);
+}
+
+// End states and flags of one pass, rounded to 16 bytes (a second pass's
+// region may follow).
+size_t pass_bytes(const gla_dims* d, int dk, int dv) {
+  return (pass_workspace(d, dk, dv) + seg_flag_bytes(d, dk, dv) + 15) / 16 * 16;
 }
 
 // Tag of one call's segment flags: a nonzero 56-bit epoch, distinct per call
@@ -138,6 +144,19 @@ uint32_t seg_wait_ticks(int64_t seg_chunks) {
   const int32_t us = g_seg_wait_us.load(std::memory_order_relaxed);
   const int64_t t = us >= 0 ? (int64_t)us * 100 : 2000 + 400 * seg_chunks;
   return (uint32_t)(t > 0xffffffffll ? 0xffffffffll : t);
+}
+
+void set_segments(ChunkArgs& a, const gla_dims* d, int dk, int dv, void* ws);
+
+// Segments, end states and flags of a pass whose region starts at ws: the
+// one-launch form where the launch allows it.
+void set_segments_flags(ChunkArgs& a, const gla_dims* d, int dk, int dv, void* ws) {
+  set_segments(a, d, dk, dv, ws);
+  if (a.nseg > 1) {
+    a.seg_flag = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + pass_workspace(d, dk, dv));
+    a.seg_tag = next_seg_tag();
+    a.seg_wait = seg_wait_ticks(a.seg_len / d->chunk);
+  }
 }
 
 void set_segments(ChunkArgs& a, const gla_dims* d, int dk, int dv, void* ws) {
@@ -224,7 +243,7 @@ const char* gla_status_string(gla_status s) {
 
 size_t gla_chunk_fwd_workspace(const gla_dims* dims) {
   if (!dims || check_dims(dims) != GLA_OK) return 0;
-  return pass_workspace(dims, (int)dims->dk, (int)dims->dv) + seg_flag_bytes(dims, (int)dims->dv);
+  return pass_bytes(dims, (int)dims->dk, (int)dims->dv);
 }
 
 void gla_set_segment_wait(int32_t microseconds) {
@@ -233,10 +252,10 @@ void gla_set_segment_wait(int32_t microseconds) {
 
 size_t gla_chunk_bwd_workspace(const gla_dims* dims) {
   if (!dims || check_dims(dims) != GLA_OK) return 0;
-  // the dq and dk passes run together (one buffer each), then the dv pass
+  // the dq and dk passes run together (one region each), then the dv pass
   // reuses the space
-  const size_t a = pass_workspace(dims, (int)dims->dk, (int)dims->dv);
-  const size_t b = 2 * pass_workspace(dims, (int)dims->dv, (int)dims->dk);
+  const size_t a = pass_bytes(dims, (int)dims->dk, (int)dims->dv);
+  const size_t b = 2 * pass_bytes(dims, (int)dims->dv, (int)dims->dk);
   return a > b ? a : b;
 }
 
@@ -288,16 +307,15 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // dq: query dO, key v, value k; state S^T from S0^T; forward time
   ChunkArgs a1 = make_pass(dims, dO, v, k, lambda, S0, 1, nullptr, dq, 0);
-  set_segments(a1, dims, DV, DK, ws);
+  set_segments_flags(a1, dims, DV, DK, ws);
   // dk: query v, key dO, value q; state G^T from dS_T^T; reverse time
   ChunkArgs a3 = make_pass(dims, v, dO, q, lambda, dS_T, 1, nullptr, dk, 1);
-  set_segments(a3, dims, DV, DK, ws);
-  if (a3.seg_state) a3.seg_state += pass_workspace(dims, DV, DK) / sizeof(float);
+  set_segments_flags(a3, dims, DV, DK, a1.nseg > 1 ? static_cast<char*>(ws) + pass_bytes(dims, DV, DK) : ws);
   // the two share the transposed shape and run in one launch
   if (gla::launch_chunk_pair(DV, DK, C, a1, a3, s) != hipSuccess) return GLA_ERR_HIP;
   // dv (and dS0): query k, key q, value dO; state G from dS_T; reverse time
   ChunkArgs a2 = make_pass(dims, k, q, dO, lambda, dS_T, 0, dS0, dv, 1);
-  set_segments(a2, dims, DK, DV, ws);
+  set_segments_flags(a2, dims, DK, DV, ws);
   if (gla::launch_chunk_pass(DK, DV, C, a2, s) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
@@ -626,13 +644,7 @@ gla_status chunk_fwd_impl(const gla_dims* dims, const gla_tensor* q, const gla_t
   }
 
   ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, o, 0);
-  set_segments(a, dims, (int)dims->dk, (int)dims->dv, ws);
-  if (a.nseg > 1) {  // one launch: the flags follow the segment states
-    a.seg_flag = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
-                                                       pass_workspace(dims, (int)dims->dk, (int)dims->dv));
-    a.seg_tag = next_seg_tag();
-    a.seg_wait = seg_wait_ticks(a.seg_len / C);
-  }
+  set_segments_flags(a, dims, (int)dims->dk, (int)dims->dv, ws);
   if (gla::launch_chunk_pass((int)dims->dk, (int)dims->dv, (int)dims->chunk, a, s) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;

@@ -279,6 +279,10 @@ struct ChunkLds {
 // returns once they are all available, and is called after this pass's
 // first tiles and entry state have been requested, so those loads and the
 // tables overlap the wait.
+// Whether a one-launch full pass requests its own loads before its wait
+// (see chunk_body): where its registers allow it.
+constexpr bool seg_early_loads(int NW, int NT, int DK) { return NW <= 8 && NT == 1 && DK <= 128; }
+
 struct NoWait {
   __device__ void operator()() const {}
 };
@@ -510,14 +514,14 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           accS[Do][s][r] = x;
         }
   };
-  // Workgroups of up to two waves per SIMD wait inside the chunk-loop
-  // prologue (below); with three, the tiles' registers held through the wait
-  // would spill.  The last segment in walk order has no state pass of its
+  // Workgroups of up to two waves per SIMD (bf16 tiles, DK <= 128) wait
+  // inside the chunk-loop prologue (below); otherwise the tiles' registers
+  // held through the wait would spill.  The last segment in walk order has no state pass of its
   // own: it requests its entry state and first tiles before it waits, while
   // the others run their state passes.  The others reach the wait just as
   // the flags are due and poll with no loads of their own in flight (a wait
   // for a load is a wait for every load issued before it).
-  constexpr bool EARLY = MRG && NW <= 8;
+  constexpr bool EARLY = MRG && seg_early_loads(NW, NT, DK);
   const bool idle_wait = seg == (REV ? 0 : nseg - 1);
   if (!EARLY || idle_wait) load_entry();
   // The segments before this one (in walk order) enter through their end
@@ -530,18 +534,20 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
     const int64_t tail = T - (int64_t)(nseg - 1) * a.seg_len;  // the last segment's length
     const float dec_full = first != seg ? lam_pow_f32(lam, (int)a.seg_len) : 1.0f;
     const float dec_last = (REV && first != seg) ? lam_pow_f32(lam, (int)tail) : dec_full;
-    if constexpr (MRG && !REV) {
+    if constexpr (MRG) {
       // States written in this launch by other workgroups: read at device
-      // scope (past this CU's cache), FB of them requested at once (all whole
-      // segments, so one power serves them), then folded in order.
+      // scope (past this CU's cache), FB of them requested at once, then
+      // folded in walk order (walk position j is segment p).
       constexpr int FB = TIGHT ? 1 : 4;
-      for (int p0 = 0; p0 < seg; p0 += FB) {
+      const int nprev = REV ? nseg - 1 - seg : seg;
+      for (int j0 = 0; j0 < nprev; j0 += FB) {
         f32x4 e[FB][DKTO][NS];
 #pragma unroll
         for (int u = 0; u < FB; ++u) {
-          if (p0 + u >= seg) continue;
+          if (j0 + u >= nprev) continue;
+          const int p = REV ? nseg - 1 - (j0 + u) : j0 + u;
           const __amdgpu_buffer_rsrc_t rs =
-              __builtin_amdgcn_make_buffer_rsrc(seg_block(p0 + u), (short)0, DK * BN * 4, 0x00020000);
+              __builtin_amdgcn_make_buffer_rsrc(seg_block(p), (short)0, DK * BN * 4, 0x00020000);
 #pragma unroll
           for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
@@ -551,13 +557,14 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
         }
 #pragma unroll
         for (int u = 0; u < FB; ++u) {
-          if (p0 + u >= seg) continue;
+          if (j0 + u >= nprev) continue;
+          const float dec = (REV && j0 + u == 0) ? dec_last : dec_full;
 #pragma unroll
           for (int Do = 0; Do < DKTO; ++Do)
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) accS[Do][s][r] = fmaf(dec_full, accS[Do][s][r], e[u][Do][s][r]);
+              for (int r = 0; r < 4; ++r) accS[Do][s][r] = fmaf(dec, accS[Do][s][r], e[u][Do][s][r]);
         }
       }
     } else {
@@ -1268,8 +1275,10 @@ __device__ __forceinline__ unsigned xcc_id() {
 // then the flag).  Its full pass then fills its tables and requests its
 // entry state and first tiles before it waits: lane p of wave 0 polls the
 // flag of walk position p, whose workgroup sits 8 (segment distance) block
-// ids earlier and so -- workgroups being dealt to the XCDs in turn -- on the
-// same XCD, sharing its L2.  A flag counts only if it carries this call's
+// ids away (earlier in forward time, later in reverse time) and so --
+// workgroups being dealt to the XCDs in turn -- on the same XCD, sharing its
+// L2.  (The launch is used only when every workgroup has a compute unit of
+// its own, so all are resident.)  A flag counts only if it carries this call's
 // tag and this XCD's id.  Any earlier state not published within a.seg_wait
 // ticks (the producer not resident, or on another XCD) is formed here by the
 // same state pass, bit for bit what its producer writes.  Then the full pass
@@ -1277,11 +1286,9 @@ __device__ __forceinline__ unsigned xcc_id() {
 // launch completes whatever the residency; the flags are cleared on exit so a
 // graph replay (same tag) starts from clear flags.
 template <int DK, int DV, int BN, int NW, int C, int NT, bool REV>
-__global__ void __launch_bounds__(NW * 64) chunk_kernel_seg(ChunkArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW>::BYTES];
-  __shared__ unsigned long long s_todo;
+__device__ __forceinline__ void seg_pass(const ChunkArgs& a, const int xb, char* const smem,
+                                         unsigned long long& s_todo) {
   constexpr int NBLK = DV / BN;
-  const int xb = blockIdx.x;
   const int nseg = a.nseg;
   const int seg = (xb >> 3) % nseg;
   const int slot2 = (xb >> 3) / nseg;
@@ -1342,16 +1349,36 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel_seg(ChunkArgs a) {
       __syncthreads();
     }
   };
-  if constexpr (NW <= 8) {
+  if constexpr (seg_early_loads(NW, NT, DK)) {
     chunk_body<DK, DV, BN, NW, C, NT, REV, false, false, false, true>(a, xb, smem, wait_entry);
   } else {
-    // (the full pass of three waves per SIMD has no registers to spare for
-    // its own loads across the wait: it starts after it)
+    // (a full pass with no registers to spare for its own loads across the
+    // wait starts after it)
     wait_entry();
     chunk_body<DK, DV, BN, NW, C, NT, REV, false, false, false, true>(a, xb, smem);
   }
   if (wi < nseg - 1 && threadIdx.x == 0)
     __hip_atomic_store(flag + seg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DK, int DV, int BN, int NW, int C, int NT, bool REV>
+__global__ void __launch_bounds__(NW * 64) chunk_kernel_seg(ChunkArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW>::BYTES];
+  __shared__ unsigned long long s_todo;
+  seg_pass<DK, DV, BN, NW, C, NT, REV>(a, blockIdx.x, smem, s_todo);
+}
+
+// The backward's two transposed passes (a0 forward time, a1 reverse time),
+// each split into segments, in one launch: workgroups [0, nb0) serve a0.
+// nb0 is a multiple of 8, so a workgroup and the earlier segments it waits
+// for still sit on one XCD.
+template <int DK, int DV, int BN, int NW, int C, int NT>
+__global__ void __launch_bounds__(NW * 64) chunk_kernel_seg_pair(ChunkArgs a0, ChunkArgs a1, int nb0) {
+  __shared__ __attribute__((aligned(16))) char smem[ChunkLds<DK, BN, C, NT, NW>::BYTES];
+  __shared__ unsigned long long s_todo;
+  const int xb = blockIdx.x;
+  if (xb < nb0) seg_pass<DK, DV, BN, NW, C, NT, false>(a0, xb, smem, s_todo);
+  else seg_pass<DK, DV, BN, NW, C, NT, true>(a1, xb - nb0, smem, s_todo);
 }
 
 // Two independent passes of one shape in one launch, the first in forward
@@ -1391,9 +1418,10 @@ static hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   // One launch only while every workgroup can hold a compute unit of its
   // own: a workgroup that waits on a segment whose workgroup is still queued
   // behind it would hold its unit idle (two launches are faster then).
-  if (a.nseg > 1 && a.seg_flag != nullptr && !a.reverse && a.cu == nullptr && a.pool == nullptr &&
+  if (a.nseg > 1 && a.seg_flag != nullptr && a.cu == nullptr && a.pool == nullptr &&
       BH * NBLK * a.nseg <= device_cus(st)) {
-    hipLaunchKernelGGL((chunk_kernel_seg<DK, DV, BN, NW, C, NT, false>), grid, block, 0, st, a);
+    if (a.reverse) hipLaunchKernelGGL((chunk_kernel_seg<DK, DV, BN, NW, C, NT, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((chunk_kernel_seg<DK, DV, BN, NW, C, NT, false>), grid, block, 0, st, a);
     return hipGetLastError();
   }
   if (a.nseg > 1) {
@@ -1417,6 +1445,11 @@ static hipError_t launch_pair(const ChunkArgs& a0, const ChunkArgs& a1, hipStrea
   const int64_t nb = groups * 8 * NBLK * a0.nseg;  // per pass (both passes share dims)
   if (nb <= 0) return hipSuccess;
   const dim3 grid((unsigned)(2 * nb)), block(NW * 64);
+  if (a0.nseg > 1 && a0.seg_flag != nullptr && a1.seg_flag != nullptr &&
+      2 * BH * NBLK * a0.nseg <= device_cus(st)) {  // one launch, as in launch_one
+    hipLaunchKernelGGL((chunk_kernel_seg_pair<DK, DV, BN, NW, C, NT>), grid, block, 0, st, a0, a1, (int)nb);
+    return hipGetLastError();
+  }
   if (a0.nseg > 1) {
     hipLaunchKernelGGL((chunk_kernel_pair<DK, DV, BN, NW, C, NT, true>), grid, block, 0, st, a0, a1, (int)nb);
     const hipError_t e = hipGetLastError();

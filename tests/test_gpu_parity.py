@@ -310,12 +310,13 @@ def test_fwd_bwd_half_decay_fp32(gla, chunk):
 # is ragged, segments are dropped by the rounding of the segment length, and
 # the reverse-time passes of the backward carry dS0 across segments.
 def segments_of(gla, B, H, T, dk, dv, chunk, bwd=False):
-    """Segments per (b, h) implied by the workspace query (fp32 end states;
-    the forward adds dv / 16 8-byte flags per state)."""
+    """Segments per (b, h) implied by the workspace query (fp32 end states
+    and dv / 16 8-byte flags per state)."""
     lib, d = gla.load_library(), ctypes.byref(gla.GlaDims(B, H, T, dk, dv, chunk))
     nws = lib.gla_chunk_bwd_workspace(d) if bwd else lib.gla_chunk_fwd_workspace(d)
-    per = dk * dv * 4 + (0 if bwd else -(-dv // 16) * 8)
-    assert nws % (B * H * per) == 0
+    per = dk * dv * 4 + -(-dv // 16) * 8
+    if not bwd:  # the backward's region also holds a second pass's flags
+        assert nws % (B * H * per) == 0
     return nws // (B * H * per)
 
 
@@ -433,6 +434,27 @@ def test_wide_tiles_fwd_bwd(gla, dtype, chunk, T):
     assert 2 <= n <= 64 and nchunks >= 8 * n
     check_fwd(gla, x, dtype, chunk)
     check_bwd(gla, x, dtype, chunk)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 96, 192, "bf16", 64), (1, 1, 1001, 16, 32, "f32", 16)])
+def test_bwd_segments_without_waiting(gla, shape):
+    """The backward's segmented passes (the paired dq/dk launch and dv) also
+    run in one launch each; with no wait at all every workgroup forms the
+    earlier end states itself: the same bits as the default wait."""
+    B, H, T, dk, dv, dtype, chunk = shape
+    flush(f"test_bwd_segments_without_waiting {shape}")
+    x = inputs.random_chunk_inputs(490 + T, B, H, T, dk, dv, dtype=dtype, dS_T=True, scale=0.3)
+    assert segments_of(gla, B, H, T, dk, dv, chunk, bwd=True) >= 2
+    base = run_bwd(gla, x, dtype, chunk)
+    try:
+        gla.set_segment_wait(0)
+        forced = run_bwd(gla, x, dtype, chunk)
+    finally:
+        gla.set_segment_wait(-1)
+    for a, b in zip(base, forced):
+        assert np.array_equal(a, b)
+    r = oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"], x["dS_T"])
+    assert max(oracle.rel_err(a, b) for a, b in zip(base, r)) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("T,chunk", [(777, 64), (1000, 128), (300, 32)])
