@@ -108,16 +108,19 @@ const char* gla_status_string(gla_status s);
  * each; page section "Challenge 1": the chunks are independent apart from the
  * state they hand on).  Each segment's end state from a zero start is written
  * to the workspace, and segment j starts from the decayed sum of the end
- * states before it.  gla_chunk_fwd does both in one launch: a workgroup
- * publishes its segment's end state with an 8-byte flag and reads the earlier
- * ones once their flags are set.  The workspace holds B*H*nseg*dk*dv fp32
- * states followed by B*H*nseg*ceil(dv/16) flags; ws must be 16-byte aligned
+ * states before it.  When the split's workgroups fit the device's compute
+ * units one each, both happen in one launch: a workgroup publishes its
+ * segment's end state with an 8-byte flag and reads the earlier ones once
+ * their flags are set (otherwise two launches).  The workspace holds
+ * B*H*nseg*dk*dv fp32 states followed by B*H*nseg*ceil(dv/16) flags, rounded
+ * up to 16 bytes; ws must be 16-byte aligned
  * (GLA_ERR_WORKSPACE otherwise).  Nothing in it needs to start at zero (a
  * flag counts only if it carries the call's own tag) and its contents are
  * not needed after the call completes. */
 size_t gla_chunk_fwd_workspace(const gla_dims* dims);
 
-/* Tuning of the one-launch segment split in gla_chunk_fwd: how long, in
+/* Tuning of the one-launch segment split (gla_chunk_fwd, gla_chunk_bwd,
+ * gla_chunk_fwd_noalloc): how long, in
  * microseconds, a workgroup waits for an earlier segment's end state before
  * forming that state itself (by the same arithmetic, so results never
  * depend on it).  Negative restores the default, about four times a
@@ -164,8 +167,10 @@ gla_status gla_chunk_fwd_noalloc(const gla_dims* dims, const gla_tensor* q, cons
                                  const gla_tensor* v, const float* lambda, const float* S0,
                                  gla_tensor* o, float* S_T, void* stream);
 
-/* Bytes of device workspace gla_chunk_bwd needs (0 if none): the largest
- * segment-state buffer of its three passes (see gla_chunk_fwd_workspace). */
+/* Bytes of device workspace gla_chunk_bwd needs (0 if none): the segment
+ * states and flags (as for gla_chunk_fwd_workspace) of its paired dq/dk
+ * passes, two regions, or of its dv pass, whichever is larger (the dv pass
+ * reuses the space).  Nothing in it needs to start at zero. */
 size_t gla_chunk_bwd_workspace(const gla_dims* dims);
 
 /* Chunked backward (page section "Challenge 3") of the scalar
