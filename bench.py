@@ -167,9 +167,9 @@ def bench_train(gla, inputs, steps, warmup, chunk=C):
 
 
 def bench_fwd_bwd_events(gla, inputs, name, reps, chunk=C):
-    """Event-timed forward and backward calls of a chunked training-shape
-    workload (the page's decay-schedule variant of the step, and the step at
-    the pages' 128-token chunk)."""
+    """Event-timed forward and backward calls of a chunked workload (the
+    page's decay-schedule variant of the training step, the step at the
+    pages' 128-token chunk, and the Laplace layer's segmented passes)."""
     import numpy as np
     import torch
 
@@ -629,6 +629,9 @@ def main():
         # the same workload at the pages' 128-token chunk (results agree up to rounding)
         extra[name + f"_fwd_chunk{C_PAGE}"] = bench_fwd_only(gla, inputs, name, reps, chunk=C_PAGE)
         log(f"  chunk {C_PAGE}: {extra[name + f'_fwd_chunk{C_PAGE}']['ms']:.3f} ms")
+    log("bench: laplace fwd+bwd (segment split in both directions)")
+    extra["laplace_fwd_bwd"] = bench_fwd_bwd_events(gla, inputs, "laplace", 50)
+    log(f"  fwd {extra['laplace_fwd_bwd']['ms_fwd']:.3f} ms  bwd {extra['laplace_fwd_bwd']['ms_bwd']:.3f} ms")
     log(f"bench: training shape fwd+bwd at the pages' {C_PAGE}-token chunk")
     extra["training_chunk128"] = bench_fwd_bwd_events(gla, inputs, "training", 20, chunk=C_PAGE)
     log(f"  fwd {extra['training_chunk128']['ms_fwd']:.3f} ms  bwd {extra['training_chunk128']['ms_bwd']:.3f} ms")
