@@ -37,11 +37,11 @@ constexpr int kCpolSc1 = 16;
 
 namespace gla {
 
-// 1 / (1 + e^-x) from the hardware base-2 exponential and reciprocal (each
+// sigmoid(x) = 1 / (1 + e^-x) from the hardware base-2 exponential and reciprocal (each
 // within about one ulp; the product x log2(e) adds |x| 2^-24 to the
 // exponent), a relative error near 1e-6 for |x| < 10.  Large negative x
 // gives 1 / inf = 0, large positive x gives 1.
-__device__ __forceinline__ float silu_gate(float x) {
+__device__ __forceinline__ float sigmoid_hw(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
@@ -960,7 +960,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
       for (int row = tid; row < CP; row += NTHR) {
         float sdot = 0.0f;
         for (int part = 0; part < PPR; ++part) sdot += sGP[row * PPR + part];
-        sGate[row] = 1.0f / (1.0f + expf(-sdot));
+        sGate[row] = sigmoid_hw(sdot);
       }
     }
 
@@ -1171,7 +1171,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
           const f32x4 t = *reinterpret_cast<const f32x4*>(&sSq[row * NWP + v4]);
           tot += (t[0] + t[1]) + (t[2] + t[3]);
         }
-        const float rstd = 1.0f / sqrtf(tot * (1.0f / DV) + a.eps);
+        const float rstd = __builtin_amdgcn_rsqf(tot * (1.0f / DV) + a.eps);  // hardware 1/sqrt, ~1 ulp
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           f32x4 y;
@@ -1210,7 +1210,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float yv = e < 4 ? y0[e] : y1[e - 4];
-            out[e] = yv * gv[e] * silu_gate(gv[e]);
+            out[e] = yv * gv[e] * sigmoid_hw(gv[e]);
           }
           if (a.o_f32) {
             const uint32_t oo = (uint32_t)row * (uint32_t)a.so_t * 4 + cv * 32;
