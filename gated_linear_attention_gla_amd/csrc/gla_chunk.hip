@@ -276,9 +276,8 @@ struct ChunkLds {
 // update runs, from a zero state, and the segment's end state goes to
 // a.seg_state.  MRG: the earlier segments' states are written in this same
 // launch, by other workgroups on this XCD, and read from L2; wait_entry()
-// returns once they are all available, and is called after this pass's
-// first tiles and entry state have been requested, so those loads and the
-// tables overlap the wait.
+// returns once they are all available (where it is called: see the chunk-loop
+// prologue).
 // Whether a one-launch full pass requests its own loads before its wait
 // (see chunk_body): where its registers allow it.
 constexpr bool seg_early_loads(int NW, int NT, int DK) { return NW <= 8 && NT == 1 && DK <= 128; }
@@ -516,11 +515,12 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int xb, cha
   };
   // Workgroups of up to two waves per SIMD (bf16 tiles, DK <= 128) wait
   // inside the chunk-loop prologue (below); otherwise the tiles' registers
-  // held through the wait would spill.  The last segment in walk order has no state pass of its
-  // own: it requests its entry state and first tiles before it waits, while
-  // the others run their state passes.  The others reach the wait just as
-  // the flags are due and poll with no loads of their own in flight (a wait
-  // for a load is a wait for every load issued before it).
+  // held through the wait would spill.  The last segment in walk order has
+  // no state pass of its own: it requests its entry state and first tiles
+  // before it waits, while the others run their state passes.  The others
+  // reach the wait just as the flags are due and poll with no loads of their
+  // own in flight (a wait for a load is a wait for every load issued before
+  // it).
   constexpr bool EARLY = MRG && seg_early_loads(NW, NT, DK);
   const bool idle_wait = seg == (REV ? 0 : nseg - 1);
   if (!EARLY || idle_wait) load_entry();
@@ -1272,9 +1272,10 @@ __device__ __forceinline__ unsigned xcc_id() {
 
 // A segment split in one launch.  Workgroup (unit, segment) first runs its
 // segment's state pass and publishes the end state (stores drained to L2,
-// then the flag).  Its full pass then fills its tables and requests its
-// entry state and first tiles before it waits: lane p of wave 0 polls the
-// flag of walk position p, whose workgroup sits 8 (segment distance) block
+// then the flag).  Its full pass then waits for the earlier segments (the
+// last segment, which has no state pass, fills its tables and requests its
+// entry state and first tiles first): lane p of wave 0 polls the flag of
+// walk position p, whose workgroup sits 8 (segment distance) block
 // ids away (earlier in forward time, later in reverse time) and so --
 // workgroups being dealt to the XCDs in turn -- on the same XCD, sharing its
 // L2.  (The launch is used only when every workgroup has a compute unit of
@@ -1306,8 +1307,8 @@ __device__ __forceinline__ void seg_pass(const ChunkArgs& a, const int xb, char*
     if (threadIdx.x == 0) __hip_atomic_store(flag + seg, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();  // LDS free for the full pass
   }
-  // Called by the full pass once its own loads are in flight: every earlier
-  // state published here, or formed by this workgroup.
+  // Called by the full pass (or before it): returns once every earlier state
+  // is published here, or formed by this workgroup.
   auto wait_entry = [&]() {
     if (threadIdx.x < 64) {  // wave 0, lane p polls the flag of walk position p
       const int p = threadIdx.x;
