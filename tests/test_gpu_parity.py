@@ -457,6 +457,51 @@ def test_bwd_segments_without_waiting(gla, shape):
     assert max(oracle.rel_err(a, b) for a, b in zip(base, r)) <= TOL[dtype]
 
 
+def test_bwd_segments_graph_replays(gla):
+    """A captured segmented backward (paired dq/dk launch and dv, one launch
+    each) replays with the tags of its capture: each replay, with new inputs
+    copied in and eager calls in between, equals the eager result bit for
+    bit."""
+    flush("test_bwd_segments_graph_replays")
+    B, H, T, chunk = 1, 2, 900, 64
+    assert segments_of(gla, B, H, T, 96, 192, chunk, bwd=True) >= 2
+    sets = [inputs.random_chunk_inputs(500 + i, B, H, T, 96, 192, dtype="bf16", dS_T=True, scale=0.3)
+            for i in range(3)]
+    q, k, v, dO = (dev(sets[0][n], "bf16") for n in ("q", "k", "v", "dO"))
+    lam, S0, dST = dev_f32(sets[0]["lam"]), dev_f32(sets[0]["S0"]), dev_f32(sets[0]["dS_T"])
+    outs = [torch.empty((B, H, T, 96), dtype=torch.float32, device="cuda"),
+            torch.empty((B, H, T, 96), dtype=torch.float32, device="cuda"),
+            torch.empty((B, H, T, 192), dtype=torch.float32, device="cuda"),
+            torch.empty((B, H, 96, 192), dtype=torch.float32, device="cuda")]
+    call = lambda: gla.chunk_bwd(q, k, v, lam, dO, S0, dST, chunk=chunk, dq=outs[0], dk=outs[1], dv=outs[2],
+                                 dS0=outs[3])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(6):
+        x = sets[i % 3]
+        for name, t in (("q", q), ("k", k), ("v", v), ("dO", dO)):
+            t.copy_(dev(x[name], "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t) for t in outs]
+        eager = gla.chunk_bwd(q, k, v, lam, dO, S0, dST, chunk=chunk, grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        for a, b in zip(got, eager):
+            assert np.array_equal(a, host(b)), f"replay {i}"
+    # the decay, S0 and dS_T stay those of the first set
+    r = oracle.bwd(x["q"], x["k"], x["v"], sets[0]["lam"], x["dO"], sets[0]["S0"], sets[0]["dS_T"])
+    assert max(oracle.rel_err(a, b) for a, b in zip(got, r)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("T,chunk", [(777, 64), (1000, 128), (300, 32)])
 def test_bwd_segments_bf16(gla, T, chunk):
     flush(f"test_bwd_segments_bf16 T={T} chunk={chunk}")
