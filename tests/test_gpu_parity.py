@@ -383,6 +383,23 @@ def test_fwd_segments_more_workgroups_than_cus(gla, B, H, T):
     check_fwd(gla, x, "bf16", 64)
 
 
+def test_fwd_segments_token_major_no_s0(gla):
+    """The one-launch segment split on token-major views (q, k, v, o stored
+    (B, T, H, d)) with no initial state and a ragged last chunk."""
+    flush("test_fwd_segments_token_major_no_s0")
+    B, H, T = 1, 4, 2000
+    x = inputs.random_chunk_inputs(510, B, H, T, 96, 192, dtype="bf16", s0=False, scale=0.3)
+    assert segments_of(gla, B, H, T, 96, 192, 64) >= 8
+    ref_o, ref_S = oracle.fwd(x["q"], x["k"], x["v"], x["lam"], None)
+    tm = lambda a: dev(np.ascontiguousarray(np.swapaxes(a, 1, 2)), "bf16").transpose(1, 2)
+    q, k, v = tm(x["q"]), tm(x["k"]), tm(x["v"])
+    o = torch.empty((B, T, H, 192), dtype=torch.float32, device="cuda").transpose(1, 2)
+    _, S = gla.chunk_fwd(q, k, v, dev_f32(x["lam"]), None, chunk=64, o=o)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(host(o), ref_o) <= TOL["bf16"]
+    assert oracle.rel_err(host(S), ref_S) <= TOL["bf16"]
+
+
 def test_fwd_segments_graph_replays(gla):
     """A captured segmented forward replays with the tag of its capture: each
     replay, with new inputs copied in and eager calls in between, must equal
@@ -455,6 +472,25 @@ def test_bwd_segments_without_waiting(gla, shape):
         assert np.array_equal(a, b)
     r = oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"], x["dS_T"])
     assert max(oracle.rel_err(a, b) for a, b in zip(base, r)) <= TOL[dtype]
+
+
+def test_bwd_segments_token_major(gla):
+    """The segmented backward with every (B, H, T, d) operand and gradient a
+    token-major view ((B, T, H, d) storage) and a ragged last chunk."""
+    flush("test_bwd_segments_token_major")
+    B, H, T = 1, 4, 2000
+    x = inputs.random_chunk_inputs(520, B, H, T, 96, 192, dtype="bf16", dS_T=True, scale=0.3)
+    assert segments_of(gla, B, H, T, 96, 192, 64, bwd=True) >= 8
+    r = oracle.bwd(x["q"], x["k"], x["v"], x["lam"], x["dO"], x["S0"], x["dS_T"])
+    tm = lambda a: dev(np.ascontiguousarray(np.swapaxes(a, 1, 2)), "bf16").transpose(1, 2)
+    out = lambda d: torch.empty((B, T, H, d), dtype=torch.float32, device="cuda").transpose(1, 2)
+    dq, dk, dv = out(96), out(96), out(192)
+    g = gla.chunk_bwd(tm(x["q"]), tm(x["k"]), tm(x["v"]), dev_f32(x["lam"]), tm(x["dO"]),
+                      dev_f32(x["S0"]), dev_f32(x["dS_T"]), chunk=64, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    errs = [oracle.rel_err(host(a), b) for a, b in zip(g, r)]
+    flush("  err dq/dk/dv/dS0 = " + " ".join(f"{e:.3e}" for e in errs))
+    assert max(errs) <= TOL["bf16"]
 
 
 def test_bwd_segments_graph_replays(gla):
