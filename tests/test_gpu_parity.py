@@ -439,6 +439,48 @@ def test_fwd_segments_graph_replays(gla):
     assert oracle.rel_err(got_o, ro) <= TOL["bf16"] and oracle.rel_err(got_S, rS) <= TOL["bf16"]
 
 
+def test_segments_on_two_streams(gla):
+    """Segmented forwards and backwards of the Laplace-layer shape enqueued on
+    two streams at once (each call with its own workspace): the one-launch
+    kernels then share the compute units, so a workgroup may find an earlier
+    segment's producer not yet resident and form that state itself.  Every
+    result must equal the same call run alone, bit for bit."""
+    flush("test_segments_on_two_streams")
+    B, H, T, chunk = 1, 16, 2048, 64
+    assert segments_of(gla, B, H, T, 96, 192, chunk) >= 2
+    sets = [inputs.random_chunk_inputs(530 + i, B, H, T, 96, 192, dtype="bf16", dS_T=True, scale=0.3)
+            for i in range(2)]
+    args = []
+    for x in sets:
+        q, k, v, dO = (dev(x[n], "bf16") for n in ("q", "k", "v", "dO"))
+        args.append((q, k, v, dev_f32(x["lam"]), dO, dev_f32(x["S0"]), dev_f32(x["dS_T"])))
+
+    def run(a):
+        q, k, v, lam, dO, S0, dST = a
+        o, S = gla.chunk_fwd(q, k, v, lam, S0, chunk=chunk, out_dtype=torch.float32)
+        g = gla.chunk_bwd(q, k, v, lam, dO, S0, dST, chunk=chunk, grad_dtype=torch.float32)
+        return (o, S) + tuple(g)
+
+    alone = []
+    for a in args:
+        alone.append([host(t) for t in run(a)])
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for rep in range(4):
+        outs = [None, None]
+        for i, s_ in enumerate(streams):
+            with torch.cuda.stream(s_):
+                outs[i] = run(args[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            for j, t in enumerate(outs[i]):
+                assert np.array_equal(host(t), alone[i][j]), f"rep {rep} stream {i} output {j}"
+    ro, rS = oracle.fwd(sets[1]["q"], sets[1]["k"], sets[1]["v"], sets[1]["lam"], sets[1]["S0"])
+    assert oracle.rel_err(alone[1][0], ro) <= TOL["bf16"] and oracle.rel_err(alone[1][1], rS) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype,chunk,T", [("bf16", 16, 8192 + 37), ("f32", 32, 16384 + 5), ("bf16", 64, 32768 - 11)])
 def test_wide_tiles_fwd_bwd(gla, dtype, chunk, T):
     """Few (b, h) units with at least 8 chunks per segment: the (96, 192)
