@@ -31,8 +31,9 @@ BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 # Chunk length of every timed call.  The output does not depend on it beyond
 # rounding (the tests check 16, 32, 64 and 128 against the oracle); the pages'
 # 128-token chunk matched Trainium's 128 SBUF partitions, while on gfx950 the
-# 64-token chunk keeps the backward's transposed passes in registers and runs
-# faster.  The 128-token chunk is timed as well and reported under "extra".
+# 64-token chunk runs faster (fewer causal-tile flops per token; at 128 the
+# library tiles the backward's transposed passes at 64 tokens anyway).  The
+# 128-token chunk is timed as well and reported under "extra".
 C = 64
 C_PAGE = 128
 DK, DV = 96, 192
@@ -634,6 +635,10 @@ def main():
     log(f"  fwd {extra['laplace_fwd_bwd']['ms_fwd']:.3f} ms  bwd {extra['laplace_fwd_bwd']['ms_bwd']:.3f} ms")
     log(f"bench: training shape fwd+bwd at the pages' {C_PAGE}-token chunk")
     extra["training_chunk128"] = bench_fwd_bwd_events(gla, inputs, "training", 20, chunk=C_PAGE)
+    # tile length of each pass at this chunk (the backward's 192 x 96 passes
+    # tile at 64 tokens: 128-token tiles fit them on no more than three waves
+    # per compute unit; results are equal up to rounding at any tile length)
+    extra["training_chunk128"]["tiles"] = {"forward": C_PAGE, "bwd_dq_dk": 64, "bwd_dv": C_PAGE}
     log(f"  fwd {extra['training_chunk128']['ms_fwd']:.3f} ms  bwd {extra['training_chunk128']['ms_bwd']:.3f} ms")
     log("bench: page decay schedule, training shape fwd+bwd")
     extra["schedule_fwd_bwd"] = bench_fwd_bwd_events(gla, inputs, "schedule", 20)
@@ -695,7 +700,8 @@ def main():
             "workload": f"training-shape chunked GLA fwd+bwd, B=8 H=16 T=2048 dk=96 dv=192 "
                         f"chunk={C}, bf16 q/k/v/dO, fp32 state",
             "chunk_note": f"chunk {C}: results are chunk-invariant up to rounding (tested at 16/32/64/128); "
-                          f"the pages' {C_PAGE}-token chunk is timed under extra.training_chunk128",
+                          f"the pages' {C_PAGE}-token chunk is timed under extra.training_chunk128 (its "
+                          f"backward's dq and dk passes tile at 64 tokens)",
             "global_batch": tr["B"], "seq_len": tr["T"], "heads": tr["H"], "dk": DK, "dv": DV,
             "chunk": C, "parallelism": "single GPU",
         },

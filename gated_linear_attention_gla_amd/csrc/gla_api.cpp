@@ -255,7 +255,15 @@ size_t gla_chunk_bwd_workspace(const gla_dims* dims) {
   // the dq and dk passes run together (one region each), then the dv pass
   // reuses the space
   const size_t a = pass_bytes(dims, (int)dims->dk, (int)dims->dv);
-  const size_t b = 2 * pass_bytes(dims, (int)dims->dv, (int)dims->dk);
+  // (the transposed passes may tile shorter than the chunk; sized for both
+  // input dtypes, as the query takes none)
+  gla_dims dt = *dims;
+  size_t b = 0;
+  for (int in_f32 = 0; in_f32 < 2; ++in_f32) {
+    dt.chunk = gla::bwd_transposed_tile((int)dims->chunk, in_f32);
+    const size_t bt = 2 * pass_bytes(&dt, (int)dims->dv, (int)dims->dk);
+    b = bt > b ? bt : b;
+  }
   return a > b ? a : b;
 }
 
@@ -305,14 +313,17 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const gla_tensor* q, const gla_te
   if (ws_bytes < need_ws || (need_ws > 0 && (ws == nullptr || !aligned16(ws)))) return GLA_ERR_WORKSPACE;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // the transposed passes' tile length (gla::bwd_transposed_tile)
+  gla_dims dt = *dims;
+  if (DV == 192 && DK == 96) dt.chunk = gla::bwd_transposed_tile(C, in_f32);
   // dq: query dO, key v, value k; state S^T from S0^T; forward time
-  ChunkArgs a1 = make_pass(dims, dO, v, k, lambda, S0, 1, nullptr, dq, 0);
-  set_segments_flags(a1, dims, DV, DK, ws);
+  ChunkArgs a1 = make_pass(&dt, dO, v, k, lambda, S0, 1, nullptr, dq, 0);
+  set_segments_flags(a1, &dt, DV, DK, ws);
   // dk: query v, key dO, value q; state G^T from dS_T^T; reverse time
-  ChunkArgs a3 = make_pass(dims, v, dO, q, lambda, dS_T, 1, nullptr, dk, 1);
-  set_segments_flags(a3, dims, DV, DK, a1.nseg > 1 ? static_cast<char*>(ws) + pass_bytes(dims, DV, DK) : ws);
+  ChunkArgs a3 = make_pass(&dt, v, dO, q, lambda, dS_T, 1, nullptr, dk, 1);
+  set_segments_flags(a3, &dt, DV, DK, a1.nseg > 1 ? static_cast<char*>(ws) + pass_bytes(&dt, DV, DK) : ws);
   // the two share the transposed shape and run in one launch
-  if (gla::launch_chunk_pair(DV, DK, C, a1, a3, s) != hipSuccess) return GLA_ERR_HIP;
+  if (gla::launch_chunk_pair(DV, DK, (int)dt.chunk, a1, a3, s) != hipSuccess) return GLA_ERR_HIP;
   // dv (and dS0): query k, key q, value dO; state G from dS_T; reverse time
   ChunkArgs a2 = make_pass(dims, k, q, dO, lambda, dS_T, 0, dS0, dv, 1);
   set_segments_flags(a2, dims, DK, DV, ws);

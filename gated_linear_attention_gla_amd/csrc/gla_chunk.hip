@@ -1589,7 +1589,9 @@ static hipError_t launch_shape(const ChunkArgs& a, const ChunkArgs* a1, hipStrea
     // bf16 inputs up to 64-token chunks: all 96 columns on 12 waves, each
     // 16-column strip shared by two waves that own 96 state rows each (three
     // waves on every SIMD); fp32 inputs: 96 columns on 6 waves; 128-token
-    // chunks: 48 columns on 3 waves with the wider register budget
+    // chunks: 48 columns on 3 waves with the wider register budget (a forward
+    // of this shape; the backward tiles these passes at 64 tokens,
+    // bwd_transposed_tile)
     if constexpr (C <= 64 && NT == 1) return launch_tiles<192, 96, 96, 12, C, NT>(a, a1, st);
     else if constexpr (C <= 64) return launch_tiles<192, 96, 96, 6, C, NT>(a, a1, st);
     else return launch_tiles<192, 96, 48, 3, C, NT>(a, a1, st);
@@ -1620,6 +1622,14 @@ bool chunk_pass_supported(int dk, int dv, int chunk, int in_f32) {
   if (small || dk == 96) return chunk <= 64;
   return chunk <= 32;
 }
+
+// Tile length of the backward's transposed passes (192-row state, 96
+// columns) for a requested chunk.  With bf16 inputs their 128-token tiles fit
+// no layout of more than three waves per compute unit (12 waves with the row
+// split need 207.5 KB of LDS; 6 waves, or 3 waves of two strips, spill
+// registers), so they tile at 64 tokens; the results are equal up to rounding
+// for every tile length.  Every other pass tiles at the chunk.
+int bwd_transposed_tile(int chunk, int in_f32) { return chunk == 128 && !in_f32 ? 64 : chunk; }
 
 static hipError_t launch_dispatch(int dk, int dv, int chunk, const ChunkArgs& a, const ChunkArgs* a1,
                                   hipStream_t st) {

@@ -135,6 +135,7 @@ hipError_t launch_chunk_pair(int dk, int dv, int chunk, const ChunkArgs& a0, con
 // they need: enough (b, h, column block, segment) units to fill the GPU.
 int chunk_segments(int64_t B, int64_t H, int64_t T, int dk, int dv, int chunk, int in_f32);
 bool chunk_pass_supported(int dk, int dv, int chunk, int in_f32);
+int bwd_transposed_tile(int chunk, int in_f32);
 // Segments for a given number of (b, h, column block) units.
 int segments_for_units(int64_t units, int64_t T, int chunk);
 // Forward with the fused output epilogue (whole heads per workgroup).

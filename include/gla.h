@@ -54,6 +54,14 @@
  *               B <= 2^24, H <= 2^16, B * H <= 2^21 and T <= 2^40
  *               (GLA_ERR_SHAPE otherwise): one launch addresses at most
  *               2^32 - 1 work-items.
+ *   Chunk       the tile length of the chunked form.  Results are equal up
+ *               to rounding for every chunk: the chunked form computes the
+ *               recurrence's sums exactly, and only the order of its
+ *               floating-point additions depends on the chunk.  Every
+ *               pass tiles at the chunk, except that at chunk 128 with bf16
+ *               inputs the backward's dq and dk passes (a 192 x 96 state)
+ *               tile at 64 tokens: their 128-token tiles fit no layout of
+ *               more than three waves per compute unit.
  *   Decay       lambda[h] must satisfy 0 <= lambda[h] <= 1 (not checked on
  *               the device); 0^0 is taken as 1.  NaN/Inf inputs propagate.
  *   Aliasing    Outputs must not share a base pointer with any input or with
@@ -170,7 +178,8 @@ gla_status gla_chunk_fwd_noalloc(const gla_dims* dims, const gla_tensor* q, cons
 /* Bytes of device workspace gla_chunk_bwd needs (0 if none): the segment
  * states and flags (as for gla_chunk_fwd_workspace) of its paired dq/dk
  * passes, two regions, or of its dv pass, whichever is larger (the dv pass
- * reuses the space).  Nothing in it needs to start at zero. */
+ * reuses the space); the dq/dk passes' segments follow their own tile length
+ * (see Chunk above).  Nothing in it needs to start at zero. */
 size_t gla_chunk_bwd_workspace(const gla_dims* dims);
 
 /* Chunked backward (page section "Challenge 3") of the scalar

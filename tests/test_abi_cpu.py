@@ -160,6 +160,19 @@ def test_workspace_segment_rule(lib):
     assert lib.gla_chunk_bwd_workspace(ctypes.byref(d)) >= lib.gla_chunk_fwd_workspace(ctypes.byref(d))
 
 
+def test_bwd_workspace_follows_transposed_tiles(lib):
+    """At chunk 128 the backward's dq and dk passes (192 x 96 state) tile at
+    64 tokens, so their segment split follows 64-token chunks.  B=1, H=16,
+    T=512: 32 (b, h) units of the paired passes, 8 chunks of 64 tokens, so 4
+    segments each (two chunks per segment), not the 2 that four 128-token
+    chunks would allow; their two regions outweigh the dv pass's."""
+    per_t = 192 * 96 * 4 + 96 // 16 * 8  # one transposed state + its flags
+    d128 = dims(B=1, H=16, Tn=512, chunk=128)
+    d64 = dims(B=1, H=16, Tn=512, chunk=64)
+    assert lib.gla_chunk_bwd_workspace(ctypes.byref(d128)) == 2 * 16 * 4 * per_t
+    assert lib.gla_chunk_bwd_workspace(ctypes.byref(d64)) == 2 * 16 * 4 * per_t
+
+
 def test_fwd_workspace_checks(lib):
     d = dims(Tn=1000, chunk=64)
     need = lib.gla_chunk_fwd_workspace(ctypes.byref(d))
