@@ -441,7 +441,12 @@ gla_status gla_decode_step_fused(int64_t N, int64_t H, int64_t dk, int64_t dv, c
 
 size_t gla_chunk_fwd_fused_workspace(const gla_dims* dims) {
   if (!dims || check_dims(dims) != GLA_OK) return 0;
-  const int nseg = gla::chunk_segments_fused(dims->B, dims->H, dims->T, (int)dims->chunk);
+  // segments of the fused tile (gla::fused_tile), sized for both input dtypes
+  int nseg = 1;
+  for (int in_f32 = 0; in_f32 < 2; ++in_f32) {
+    const int n = gla::chunk_segments_fused(dims->B, dims->H, dims->T, gla::fused_tile((int)dims->chunk, in_f32));
+    nseg = n > nseg ? n : nseg;
+  }
   if (nseg <= 1) return 0;
   return (size_t)dims->B * dims->H * nseg * dims->dk * dims->dv * sizeof(float);
 }
@@ -459,8 +464,9 @@ gla_status gla_chunk_fwd_fused(const gla_dims* dims, const gla_tensor* q, const 
       g->dtype != q->dtype)
     return GLA_ERR_DTYPE;
   const int in_f32 = q->dtype == GLA_F32;
-  if (!gla::chunk_fused_supported((int)dims->dk, (int)dims->dv, (int)dims->chunk, in_f32))
-    return GLA_ERR_UNSUPPORTED;
+  // the tile length (gla::fused_tile: 128-token chunks tile at 64 tokens)
+  const int64_t CT = gla::fused_tile((int)dims->chunk, in_f32);
+  if (!gla::chunk_fused_supported((int)dims->dk, (int)dims->dv, (int)CT, in_f32)) return GLA_ERR_UNSUPPORTED;
   const bool need = T > 0;
   const int64_t DK = dims->dk, DV = dims->dv, C = dims->chunk;
   if ((st = check_view(q, B, H, T, DK, C, need)) != GLA_OK) return st;
@@ -478,15 +484,15 @@ gla_status gla_chunk_fwd_fused(const gla_dims* dims, const gla_tensor* q, const 
   if (ws_bytes < need_ws || (need_ws > 0 && (ws == nullptr || !aligned16(ws)))) return GLA_ERR_WORKSPACE;
 
   ChunkArgs a = make_pass(dims, q, k, v, lambda, S0, 0, S_T, y, 0);
-  a.nseg = gla::chunk_segments_fused(B, H, T, (int)C);
-  a.seg_len = a.nseg > 1 ? seg_len_for(T, C, a.nseg) : (T > 0 ? T : 1);
+  a.nseg = gla::chunk_segments_fused(B, H, T, (int)CT);
+  a.seg_len = a.nseg > 1 ? seg_len_for(T, CT, a.nseg) : (T > 0 ? T : 1);
   a.seg_state = a.nseg > 1 ? static_cast<float*>(ws) : nullptr;
   a.gz = g->data;
   a.sg_b = g->stride_b; a.sg_h = g->stride_h; a.sg_t = g->stride_t;
   a.aug = aug;
   a.gamma = gamma;
   a.eps = eps;
-  if (gla::launch_chunk_fused((int)DK, (int)DV, (int)C, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  if (gla::launch_chunk_fused((int)DK, (int)DV, (int)CT, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
 }

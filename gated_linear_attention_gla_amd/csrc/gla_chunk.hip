@@ -1485,6 +1485,11 @@ bool chunk_fused_supported(int dk, int dv, int chunk, int in_f32) {
   return chunk == 16 || chunk == 32 || chunk == 64;
 }
 
+// Tile length of the fused forward for a requested chunk: at 128 tokens its
+// fp32 output staging (98 KB) does not fit beside the tiles, so bf16 inputs
+// tile at 64 tokens (results equal up to rounding for every tile length).
+int fused_tile(int chunk, int in_f32) { return chunk == 128 && !in_f32 ? 64 : chunk; }
+
 int chunk_segments_fused(int64_t B, int64_t H, int64_t T, int chunk) {
   return segments_for_units(B * H, T, chunk);
 }

@@ -141,6 +141,7 @@ int segments_for_units(int64_t units, int64_t T, int chunk);
 // Forward with the fused output epilogue (whole heads per workgroup).
 bool chunk_fused_supported(int dk, int dv, int chunk, int in_f32);
 int chunk_segments_fused(int64_t B, int64_t H, int64_t T, int chunk);
+int fused_tile(int chunk, int in_f32);
 hipError_t launch_chunk_fused(int dk, int dv, int chunk, const ChunkArgs& a, hipStream_t st);
 hipError_t launch_decode(int dk, int dv, const DecodeArgs& a, hipStream_t st);
 bool decode_supported(int dk, int dv);

@@ -60,8 +60,9 @@
  *               floating-point additions depends on the chunk.  Every
  *               pass tiles at the chunk, except that at chunk 128 with bf16
  *               inputs the backward's dq and dk passes (a 192 x 96 state)
- *               tile at 64 tokens: their 128-token tiles fit no layout of
- *               more than three waves per compute unit.
+ *               tile at 64 tokens, their 128-token tiles fitting no layout
+ *               of more than three waves per compute unit, and so does
+ *               gla_chunk_fwd_fused (its output staging does not fit).
  *   Decay       lambda[h] must satisfy 0 <= lambda[h] <= 1 (not checked on
  *               the device); 0^0 is taken as 1.  NaN/Inf inputs propagate.
  *   Aliasing    Outputs must not share a base pointer with any input or with
@@ -235,9 +236,12 @@ int gla_decode_workgroups_per_state(int64_t N, int64_t H, int64_t dk, int64_t dv
  *   aug    fp32 [H][dk];  gamma fp32 [H][dv] (a tier's RMSNorm weight,
  *          repeated for each head of the tier);  eps >= 0 (GLA_ERR_SHAPE
  *          otherwise)
- * Shapes: (dk, dv) in {(96, 192), (16, 32)}; chunk in {16, 32, 64} (fp32
- * inputs at (96, 192): 16 or 32).  Workspace from
- * gla_chunk_fwd_fused_workspace (segment states, as for gla_chunk_fwd). */
+ * Shapes: (dk, dv) in {(96, 192), (16, 32)}; chunk in {16, 32, 64, 128}
+ * (fp32 inputs: 16 or 32 at (96, 192), up to 64 at (16, 32)).  With bf16
+ * inputs chunk 128 tiles at 64 tokens: a 128-token tile's fp32 output
+ * staging does not fit beside its tiles (results are equal up to rounding,
+ * see Chunk above).  Workspace from gla_chunk_fwd_fused_workspace (segment
+ * states, as for gla_chunk_fwd). */
 size_t gla_chunk_fwd_fused_workspace(const gla_dims* dims);
 gla_status gla_chunk_fwd_fused(const gla_dims* dims, const gla_tensor* q, const gla_tensor* k,
                                const gla_tensor* v, const float* lambda, const float* S0,

@@ -173,6 +173,14 @@ def test_bwd_workspace_follows_transposed_tiles(lib):
     assert lib.gla_chunk_bwd_workspace(ctypes.byref(d64)) == 2 * 16 * 4 * per_t
 
 
+def test_fused_workspace_follows_its_tile(lib):
+    """The fused forward tiles 128-token chunks at 64 tokens (bf16), so its
+    segment split at chunk 128 is the one of chunk 64: B=1, H=16, T=2048
+    gives 16 (b, h) units, 32 chunks of 64 tokens and 16 segments."""
+    q = lambda c: lib.gla_chunk_fwd_fused_workspace(ctypes.byref(dims(B=1, H=16, Tn=2048, chunk=c)))
+    assert q(128) == q(64) == 16 * 16 * 96 * 192 * 4
+
+
 def test_fwd_workspace_checks(lib):
     d = dims(Tn=1000, chunk=64)
     need = lib.gla_chunk_fwd_workspace(ctypes.byref(d))
@@ -390,7 +398,15 @@ def test_fused_entry_points_reject_bad_arguments(lib):
     assert call(aug=None) == NULL
     assert call(eps=-1.0) == SHAPE
     assert call(eps=float("nan")) == SHAPE
-    assert call(dd=dims(chunk=128)) == UNSUP
+    assert call(dd=dims(chunk=256)) == UNSUP
+    # fp32 inputs at (96, 192) fuse only 16- and 32-token tiles
+    q32, k32, v32, _ = views()
+    g32 = T(0x500000, gb.GLA_F32, sb=2 * 64 * 192, sh=64 * 192, st=192)
+    for x in (q32, k32, v32):
+        x.dtype = gb.GLA_F32
+    for c in (64, 128):
+        assert lib.gla_chunk_fwd_fused(ref(dims(chunk=c)), ref(q32), ref(k32), ref(v32), 0x9000, None, ref(g32),
+                                       0xA000, 0xB000, ctypes.c_float(1e-6), ref(o), None, None, 0, None) == UNSUP
     assert call(aug=0xA004) == STRIDE
     assert call(y=T(0x500000, sb=2 * 64 * 192, sh=64 * 192, st=192)) == ALIAS
     # decode with the epilogue

@@ -63,7 +63,7 @@ def test_fused_full_dims_fp32(gla, chunk):
     check(gla, x, e, "f32", chunk)
 
 
-@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("chunk", [32, 64, 128])
 def test_fused_laplace_bf16(gla, chunk):
     flush(f"test_fused_laplace_bf16 chunk={chunk}")
     x = inputs.make_chunk_inputs("laplace", T=700)
