@@ -47,8 +47,8 @@
  *               states (S0, S_T, dS_T, dS0, decode S) and lambda are fp32,
  *               dense row-major [B][H][dk][dv] (dk rows of dv).
  *   Shapes      (dk, dv) in {(96, 192), (16, 32)}; chunk in {16, 32, 64, 128}.
- *               fp32 inputs at (96, 192) need chunk <= 64 for the forward and
- *               chunk <= 32 for the backward.  Other combinations return
+ *               fp32 inputs need chunk <= 64, and chunk <= 32 for the
+ *               backward at (96, 192).  Other combinations return
  *               GLA_ERR_UNSUPPORTED.  B, H >= 1; T >= 0 (T = 0 copies the
  *               state through); T need not be a multiple of chunk.
  *               B <= 2^24, H <= 2^16, B * H <= 2^21 and T <= 2^40
